@@ -1,0 +1,180 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  * attn_fwd on the causal prefill workload B=4, H=32, S=8192, d=128, bf16
+    (the tiled forward with online softmax), and
+  * attn_verify on the speculative-verify workload (8 sequences, 32 query
+    heads over 8 KV heads, 5 new tokens each, d=128, bf16, ragged caches of
+    1024..16384 + 5 keys): split-KV kernel plus merge kernel.
+
+Inputs are resident in HBM before the timed region.  The verify cache is
+rotated over 4 independent copies so that a call cannot be served from the
+256 MB last-level cache left warm by the previous call.  Per-call durations
+come from HIP events recorded on the stream the library launches on.
+
+Prints one JSON line: value = prefill TFLOP/s (causal FLOPs halved:
+2*B*H*S^2*d per call); the verify throughput (algorithmic bytes: K and V of
+every valid cache row plus Q, O and LSE, per call) rides along under
+"verify".  The CPU-baseline leg times the fp64 oracle on a bounded sample of
+the prefill workload (whole heads) on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal prefill TFLOP/s @S=8192,d=128 (% MFMA peak); verify KV GB/s (% HBM)"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def verify_algorithmic_bytes(w, seqlens: np.ndarray) -> int:
+    kv = int(seqlens.sum()) * w.Hkv * w.d * 2 * 2          # K and V rows that are read, bf16
+    qo = 2 * w.B * w.H * w.kq * w.d * 2                    # Q read, O written
+    lse = w.B * w.H * w.kq * 4
+    return kv + qo + lse
+
+
+def cpu_baseline(w, max_seconds_hint: float = 20.0) -> dict:
+    """The oracle, as it is, on whole heads of the prefill workload."""
+    from exact_attention_04_amd import synth
+    from oracle import ref_attention as ref
+
+    cores = min(16, ref.default_workers())
+    n_heads = min(w.B * w.H, 2 * cores)
+    q, k, v = synth.prefill_inputs(w, "cpu")
+    heads = [(i // w.H, i % w.H) for i in range(n_heads)]
+    qn, kn, vn = synth.to_f64(q[:1 + heads[-1][0]]), synth.to_f64(k[:1 + heads[-1][0]]), synth.to_f64(v[:1 + heads[-1][0]])
+    log(f"cpu baseline: oracle on {n_heads} heads x {w.Sq} rows with {cores} threads")
+    t0 = time.perf_counter()
+    ref.attention(qn, kn, vn, w.causal, w.scale, heads=heads, workers=cores)
+    dt = time.perf_counter() - t0
+    flops = n_heads * (2.0 * w.Sq * w.Sk * w.d)  # causal convention: half of 4*S^2*d
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_heads} of {w.B * w.H} (batch, head) pairs of {w.name}, all {w.Sq} query rows, "
+                      f"fp64 materialised rows; {dt:.1f} s wall; causal FLOPs halved like the GPU figure"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the attention path "
+              f"shards by head with no exchange, so N GPUs run N independent copies)", file=sys.stderr)
+        return 2
+
+    import torch
+    from exact_attention_04_amd import binding, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    wp = synth.CAUSAL_BF16_S8192
+    wv = synth.VERIFY_BF16
+
+    # ---- inputs resident in HBM
+    q, k, v = synth.prefill_inputs(wp, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((wp.B, wp.H, wp.Sq), dtype=torch.float32, device=dev)
+    vq, vk, vv, vsl = synth.verify_inputs(wv, dev)
+    seqlens = vsl.cpu().numpy()
+    max_len = int(seqlens.max())
+    n_rot = 4
+    caches = [(vk, vv)] + [(vk.clone(), vv.clone()) for _ in range(n_rot - 1)]
+    vo = torch.empty_like(vq)
+    vlse = torch.empty((wv.B, wv.H, wv.kq), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(16, binding.attn_verify_workspace_bytes(wv.B, wv.H, wv.kq, wv.d, max_len)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def prefill():
+        binding.fwd(q, k, v, causal=True, scale=wp.scale, out=o, lse=lse)
+
+    def verify(i):
+        kc, vc = caches[i % n_rot]
+        binding.verify(vq, kc, vc, vsl, max_len, scale=wv.scale, out=vo, lse=vlse, workspace=ws)
+
+    for i in range(args.warmup):
+        prefill()
+        verify(i)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record(stream)
+        prefill()
+        e[1].record(stream)
+        e[2].record(stream)
+        verify(i)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    pre_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    ver_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    flops = wp.flops()
+    tflops = flops / (pre_ms.mean() * 1e-3) / 1e12
+    vbytes = verify_algorithmic_bytes(wv, seqlens)
+    gbps = vbytes / (ver_ms.mean() * 1e-3) / 1e9
+    log(f"device {props.name} CUs={props.multi_processor_count}")
+    log(f"prefill: mean {pre_ms.mean():.3f} ms (p10 {np.percentile(pre_ms, 10):.3f}, p90 {np.percentile(pre_ms, 90):.3f})"
+        f" -> {tflops:.1f} TFLOP/s = {100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak")
+    log(f"verify: mean {ver_ms.mean() * 1e3:.1f} us (p10 {np.percentile(ver_ms, 10) * 1e3:.1f}, "
+        f"p90 {np.percentile(ver_ms, 90) * 1e3:.1f}) -> {gbps:.0f} GB/s = {100 * gbps / PEAK_HBM_GBPS:.1f}% of HBM")
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wp.name} + {wv.name}",
+                   "prefill": {"B": wp.B, "H": wp.H, "Hkv": wp.Hkv, "S": wp.Sq, "d": wp.d, "causal": True,
+                               "seed": wp.seed},
+                   "verify": {"B": wv.B, "H": wv.H, "Hkv": wv.Hkv, "kq": wv.kq, "d": wv.d, "seed": wv.seed,
+                              "seqlens_k": seqlens.tolist(), "cache_copies_rotated": n_rot}},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "verify": {"value": round(gbps, 1), "unit": "GB/s", "us_per_call": round(ver_ms.mean() * 1e3, 2),
+                   "algorithmic_bytes": vbytes,
+                   "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None}},
+        "prefill_ms": round(float(pre_ms.mean()), 4),
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wp)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

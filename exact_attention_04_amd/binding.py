@@ -1,0 +1,139 @@
+"""ctypes binding of libattn.so.
+
+Argument marshalling only: torch tensors supply device memory and the current
+stream, every step of the computation runs in the library's HIP kernels.  The
+raw entry points keep the C names (``attn_fwd``, ``attn_verify``,
+``attn_verify_workspace_bytes``, ``attn_strerror``); ``fwd`` and ``verify``
+are tensor-level conveniences over them.  Importing this module raises if the
+library has not been built: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+ATTN_F32 = 0
+ATTN_BF16 = 1
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARG = -1
+ATTN_ERR_UNSUPPORTED = -2
+ATTN_ERR_WORKSPACE = -3
+ATTN_ERR_HIP = -4
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m exact_attention_04_amd.build`")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+lib.attn_fwd.restype = _i
+lib.attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp]
+lib.attn_verify_workspace_bytes.restype = _sz
+lib.attn_verify_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
+lib.attn_verify.restype = _i
+lib.attn_verify.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]
+lib.attn_strerror.restype = ctypes.c_char_p
+lib.attn_strerror.argtypes = [_i]
+
+EXPORTED = ("attn_fwd", "attn_verify", "attn_verify_workspace_bytes", "attn_strerror")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {attn_strerror(code)} (code {code})")
+        self.code = code
+
+
+def attn_strerror(code: int) -> str:
+    return lib.attn_strerror(code).decode()
+
+
+def attn_fwd(q, k, v, o, lse, B, H, Hkv, Sq, Sk, d, causal, scale, dtype, stream) -> int:
+    """Raw C entry point (device pointers as ints); returns the ATTN_* code."""
+    return lib.attn_fwd(q, k, v, o, lse, B, H, Hkv, Sq, Sk, d, int(causal), float(scale), dtype, stream)
+
+
+def attn_verify_workspace_bytes(B, H, kq, d, max_seqlen_k) -> int:
+    return int(lib.attn_verify_workspace_bytes(B, H, kq, d, max_seqlen_k))
+
+
+def attn_verify(q, k_cache, v_cache, seqlens_k, max_seqlen_k, cache_stride, o, lse, B, H, Hkv, kq, d,
+                scale, dtype, workspace, workspace_bytes, stream) -> int:
+    """Raw C entry point (device pointers as ints); returns the ATTN_* code."""
+    return lib.attn_verify(q, k_cache, v_cache, seqlens_k, max_seqlen_k, cache_stride, o, lse, B, H, Hkv,
+                           kq, d, float(scale), dtype, workspace, workspace_bytes, stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr() or None
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+        scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+        lse: Optional[torch.Tensor] = None, want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """O, LSE of attention over q [B,H,Sq,d], k/v [B,Hkv,Sk,d] on the current stream."""
+    B, H, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    rc = attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, Sq, Sk, d,
+                  causal, scale, _dtype_code(q), _stream(q))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_fwd")
+    return out, lse
+
+
+def verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seqlens_k: torch.Tensor,
+           max_seqlen_k: int, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+           want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """O, LSE of q [B,H,kq,d] against caches [B,Hkv,stride,d] with int32 seqlens_k [B]."""
+    B, H, kq, d = q.shape
+    Hkv, stride = k_cache.shape[1], k_cache.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, kq), dtype=torch.float32, device=q.device)
+    need = attn_verify_workspace_bytes(B, H, kq, d, max_seqlen_k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if seqlens_k.dtype != torch.int32:
+        raise TypeError("seqlens_k must be int32")
+    rc = attn_verify(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens_k), max_seqlen_k, stride,
+                     _ptr(out), _ptr(lse), B, H, Hkv, kq, d, scale, _dtype_code(q),
+                     _ptr(workspace), workspace.numel(), _stream(q))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_verify")
+    return out, lse

@@ -1,0 +1,116 @@
+// C ABI of the attention library: argument validation and dispatch.
+//
+// Every check runs on the host before the first HIP call, so a rejected call
+// has no side effect and the checks can be exercised without a GPU.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/attn.h"
+#include "launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// A pointer must be non-null and aligned unless its tensor is empty.
+bool ptr_ok(const void* p, size_t elems) { return elems == 0 || (p != nullptr && aligned16(p)); }
+
+bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
+
+constexpr size_t kMaxElems = (size_t)1 << 40;  // keeps every index product in 64-bit range
+
+}  // namespace
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int Hkv, int Sq, int Sk, int d,
+                        int causal, float scale, int dtype, void* stream) {
+  if (B < 0 || Sq < 0 || Sk < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || d < 1) return ATTN_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  const size_t nq = (size_t)B * H * Sq * d;
+  const size_t nk = (size_t)B * Hkv * Sk * d;
+  if (nq > kMaxElems || nk > kMaxElems) return ATTN_ERR_INVALID_ARG;
+  if ((size_t)B * H * (size_t)((Sq + 127) / 128) > 0x7fffffffu) return ATTN_ERR_INVALID_ARG;
+  if (!ptr_ok(q, nq) || !ptr_ok(o, nq) || !ptr_ok(k, nk) || !ptr_ok(v, nk)) return ATTN_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned4(lse)) return ATTN_ERR_INVALID_ARG;
+  if (nq == 0) return ATTN_OK;
+
+  attn::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.Sq = Sq;
+  a.Sk = Sk;
+  a.d = d;
+  a.causal = causal != 0;
+  a.scale = scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = dtype == ATTN_BF16 ? attn::launch_fwd_bf16(a, s) : attn::launch_fwd_f32(a, s);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+extern "C" size_t attn_verify_workspace_bytes(int B, int H, int kq, int d, int max_seqlen_k) {
+  if (B < 0 || H < 1 || kq < 1 || (d != 64 && d != 128) || max_seqlen_k < 0) return 0;
+  return attn::verify_workspace_bytes(B, H, kq, d, max_seqlen_k);
+}
+
+extern "C" int attn_verify(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* seqlens_k, int max_seqlen_k, int cache_stride,
+                           void* o, float* lse, int B, int H, int Hkv, int kq, int d,
+                           float scale, int dtype, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (B < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || kq < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
+  if (max_seqlen_k < 0 || cache_stride < 0 || max_seqlen_k > cache_stride) return ATTN_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if ((H / Hkv) * kq > 32) return ATTN_ERR_UNSUPPORTED;
+  const size_t nq = (size_t)B * H * kq * d;
+  const size_t nk = (size_t)B * Hkv * cache_stride * d;
+  if (nq > kMaxElems || nk > kMaxElems) return ATTN_ERR_INVALID_ARG;
+  if (!ptr_ok(q, nq) || !ptr_ok(o, nq) || !ptr_ok(k_cache, nk) || !ptr_ok(v_cache, nk))
+    return ATTN_ERR_INVALID_ARG;
+  if (B > 0 && (seqlens_k == nullptr || !aligned4(seqlens_k))) return ATTN_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned4(lse)) return ATTN_ERR_INVALID_ARG;
+  const size_t need = attn::verify_workspace_bytes(B, H, kq, d, max_seqlen_k);
+  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (need > 0 && (workspace == nullptr || !aligned16(workspace))) return ATTN_ERR_INVALID_ARG;
+  if (nq == 0) return ATTN_OK;
+
+  attn::VerifyArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.seqlens = seqlens_k;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.kq = kq;
+  a.d = d;
+  a.max_seqlen_k = max_seqlen_k;
+  a.cache_stride = cache_stride;
+  a.scale = scale;
+  a.workspace = workspace;
+  const hipError_t e = attn::launch_verify_bf16(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+extern "C" const char* attn_strerror(int code) {
+  switch (code) {
+    case ATTN_OK: return "success";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument (null/misaligned pointer, size, or scale)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration (head dim, dtype, or query packing)";
+    case ATTN_ERR_WORKSPACE: return "workspace too small";
+    case ATTN_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown error code";
+  }
+}

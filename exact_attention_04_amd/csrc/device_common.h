@@ -1,0 +1,77 @@
+// Device-side building blocks shared by the attention kernels (gfx950 only).
+//
+// Matrix-core conventions used throughout (v_mfma_f32_32x32x16_bf16, wave64):
+//   * A operand (32 x 16): lane l holds row m = l % 32, eight k values
+//     selected by the lane half h = l / 32;
+//   * B operand (16 x 32): lane l holds column n = l % 32, the eight k values
+//     of the same half h;
+//   * C/D (32 x 32 fp32, 16 registers): register r of lane l holds
+//     row 8*(r/4) + 4*h + r%4, column l % 32.
+// A and B always map (half, item) to the contraction index the same way, so
+// the order of the contraction inside one instruction never matters.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma_32x32x16_bf16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// 2^x on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// log2(x) (v_log_f32).
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Round-to-nearest-even fp32 -> bf16 of two values, packed lo | hi << 16
+// (the compiler emits v_cvt_pk_bf16_f32 for this).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v.x = (__bf16)lo;
+  v.y = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Low 16-bit halves of a and b packed as (a.lo, b.lo); high halves likewise.
+__device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// Value of lane (l ^ 32) -- the other half of the wave.
+__device__ __forceinline__ float swap_halves(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void store16(void* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// Workgroup index remapped so that the workgroups the hardware sends to one
+// XCD (dispatch is round-robin over the 8 XCDs) get consecutive logical ids:
+// neighbouring tiles of one head then share that XCD's L2.
+__device__ __forceinline__ int xcd_grouped_block(int bid, int nblocks) {
+  constexpr int kXcds = 8;
+  if (nblocks % kXcds != 0) return bid;
+  return (bid % kXcds) * (nblocks / kXcds) + bid / kXcds;
+}
+
+}  // namespace attn

@@ -1,0 +1,43 @@
+// Host-side launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;  // may be null
+  int B, H, Hkv, Sq, Sk, d;
+  int causal;
+  float scale;
+};
+
+struct VerifyArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* seqlens;
+  void* o;
+  float* lse;  // may be null
+  int B, H, Hkv, kq, d;
+  int max_seqlen_k, cache_stride;
+  float scale;
+  void* workspace;
+};
+
+// Each returns hipSuccess or the launch error.
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+hipError_t launch_verify_bf16(const VerifyArgs& a, hipStream_t s);
+
+// Keys per split-KV chunk of the verify path and the workspace it implies.
+int verify_chunk_keys();
+size_t verify_workspace_bytes(int B, int H, int kq, int d, int max_seqlen_k);
+
+}  // namespace attn

@@ -1,0 +1,122 @@
+/*
+ * Exact scaled-dot-product attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libattn.so.  Plain pointers and sizes only; every pointer argument
+ * except those named "host" is a device address.  The library never
+ * allocates or frees memory, never synchronises, and keeps no state between
+ * calls: it is re-entrant, and calls on different streams may overlap.  Work
+ * is enqueued on `stream` (a hipStream_t; NULL means the default stream) and
+ * the function returns once it is launched.  Inputs must stay unchanged and
+ * outputs untouched until the stream reaches the call.
+ *
+ * Layouts are contiguous, row-major, with the head dimension innermost.
+ *
+ * Error convention: 0 on success, a negative ATTN_ERR_* code otherwise.
+ * Every check except ATTN_ERR_HIP runs on the host before any HIP call, so a
+ * rejected call has no side effect.  attn_strerror() names a code.
+ */
+#ifndef EXACT_ATTN_H
+#define EXACT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of Q, K, V and O. */
+#define ATTN_F32 0  /* IEEE fp32 */
+#define ATTN_BF16 1 /* bfloat16; accumulation is always fp32 */
+
+#define ATTN_OK 0
+#define ATTN_ERR_INVALID_ARG (-1) /* null or misaligned pointer, bad size, bad scale */
+#define ATTN_ERR_UNSUPPORTED (-2) /* head dim not 64/128, dtype, verify query packing */
+#define ATTN_ERR_WORKSPACE (-3)   /* verify workspace smaller than required */
+#define ATTN_ERR_HIP (-4)         /* the kernel launch failed */
+
+/*
+ * attn_fwd -- O = softmax(scale * Q K^T + mask) V, and per-row LSE.
+ *
+ * Definition: "Warmup Guide -- Inference Optimization at Depth", Ch.1
+ * (S = QK^T, P = softmax(S), O = PV) with Ch.4's 1/sqrt(d) scale and causal
+ * mask; computed as in its Ch.4 / Ch.3 (tiles of Q, K/V streamed on chip,
+ * online softmax with running max and denominator, one normalised write per
+ * row block; the score matrix is never stored) and as the Mechanics section
+ * of "FlashAttention, speculative decoding, quantisation and parallelism"
+ * sketches it.  The result equals the plain definition up to floating-point
+ * rounding.
+ *
+ *   q    [B, H,   Sq, d]  dtype           (read)
+ *   k, v [B, Hkv, Sk, d]  dtype           (read)
+ *   o    [B, H,   Sq, d]  dtype           (written)
+ *   lse  [B, H,   Sq]     fp32            (written; may be NULL to skip)
+ *
+ * Query head h reads KV head h / (H / Hkv) (grouped-query attention).
+ * causal != 0: key j is visible to query i iff j <= i + Sk - Sq (the mask is
+ * aligned to the bottom-right corner; for Sq == Sk this is j <= i).
+ * scale must be finite and > 0 (normally 1/sqrt(d)).
+ * lse = ln(sum_j exp(scale * q_i.k_j)) over the visible keys, natural log of
+ * the scaled logits.  A row with no visible key gets O = 0 and lse = -inf.
+ * Rounding: O is rounded to nearest-even from fp32.  In the bf16 path the
+ * probabilities are rounded to bf16 before the P.V product and the
+ * denominator is summed from the unrounded fp32 values.
+ *
+ * Sizes: B, Sq, Sk >= 0 (zero sizes are allowed; B*Sq == 0 is a no-op and a
+ * pointer whose tensor is empty may be NULL); H, Hkv >= 1 with H % Hkv == 0;
+ * d in {64, 128}.  Pointers must be 16-byte aligned (lse: 4-byte).
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int Hkv, int Sq, int Sk, int d,
+             int causal, float scale, int dtype, void* stream);
+
+/*
+ * attn_verify_workspace_bytes -- bytes of device workspace attn_verify needs
+ * for these sizes (fp32 partial outputs and LSEs of the key chunks plus
+ * alignment).  Returns 0 for invalid sizes.
+ */
+size_t attn_verify_workspace_bytes(int B, int H, int kq, int d, int max_seqlen_k);
+
+/*
+ * attn_verify -- attention of kq new query tokens per sequence against a
+ * ragged KV cache: the verify step of speculative decoding, where the target
+ * model scores all drafted positions in one pass ("FlashAttention,
+ * speculative decoding, quantisation and parallelism", Mechanics /
+ * Speculative decoding).  Computed as Flash-Decoding ("Making Decode Fast",
+ * §5: split the keys across compute units, then a small final combine): a
+ * split kernel writes a partial (O_c, LSE_c) per key chunk and a merge kernel
+ * combines them with the two-block update of "Warmup Guide", Ch.3.
+ *
+ *   q                 [B, H, kq, d]                 bf16 (read)
+ *   k_cache, v_cache  [B, Hkv, cache_stride, d]     bf16 (read; only the first
+ *                                                   seqlens_k[b] rows of each
+ *                                                   (b, head) are read)
+ *   seqlens_k         [B] int32 (device): valid keys of sequence b, which
+ *                     include the kq new tokens' keys as the last kq rows
+ *   o                 [B, H, kq, d]                 bf16 (written)
+ *   lse               [B, H, kq]                    fp32 (written; may be NULL)
+ *   workspace         attn_verify_workspace_bytes(...) bytes, caller-owned,
+ *                     16-byte aligned, contents ignored
+ *
+ * Query i of sequence b sees keys [0, seqlens_k[b] - kq + i] (causal among
+ * the new tokens, bottom-right aligned).  max_seqlen_k is a host-side bound
+ * with max_seqlen_k >= every seqlens_k[b] and max_seqlen_k <= cache_stride;
+ * device values above it are clamped to it, negative values to 0.  Rows with
+ * no visible key get O = 0 and lse = -inf.  dtype must be ATTN_BF16;
+ * d in {64, 128}; (H / Hkv) * kq <= 32 (the query rows that share one KV head
+ * are packed into one 32-row matrix tile).
+ */
+int attn_verify(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* seqlens_k, int max_seqlen_k, int cache_stride,
+                void* o, float* lse, int B, int H, int Hkv, int kq, int d,
+                float scale, int dtype, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* Static, human-readable name of an ATTN_* return code. */
+const char* attn_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTN_H */

@@ -38,7 +38,7 @@ from __future__ import annotations
 
 import math
 import os
-from concurrent.futures import ProcessPoolExecutor
+from concurrent.futures import ThreadPoolExecutor
 from typing import Iterable, List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -101,14 +101,14 @@ def _one_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, scale: 
     return out, lse
 
 
-def _head_task(args):
-    q, k, v, causal, scale, rows, Sq, row_chunk = args
-    try:  # one BLAS thread per worker process
+def _blas_one_thread():
+    """Context limiting BLAS to one thread per worker (when threadpoolctl exists)."""
+    try:
         from threadpoolctl import threadpool_limits
-        with threadpool_limits(1):
-            return _one_head(q, k, v, causal, scale, rows, Sq, row_chunk)
+        return threadpool_limits(1)
     except ImportError:  # pragma: no cover
-        return _one_head(q, k, v, causal, scale, rows, Sq, row_chunk)
+        import contextlib
+        return contextlib.nullcontext()
 
 
 def attention(q, k, v, causal: bool, scale: float, rows: Optional[Sequence[int]] = None,
@@ -148,8 +148,10 @@ def attention(q, k, v, causal: bool, scale: float, rows: Optional[Sequence[int]]
         qs = q[b, h] if rows_arr is None else q[b, h][rows_arr]
         tasks.append((qs, k[b, g], v[b, g], causal, float(scale), rows_arr, Sq, row_chunk))
     if workers > 1 and len(tasks) > 1:
-        with ProcessPoolExecutor(max_workers=workers) as ex:
-            results = list(ex.map(_head_task, tasks))
+        # worker threads (NumPy releases the GIL inside its kernels), one BLAS
+        # thread each; no process is forked
+        with _blas_one_thread(), ThreadPoolExecutor(max_workers=workers) as ex:
+            results = list(ex.map(lambda t: _one_head(*t), tasks))
     else:
         results = [_one_head(*t) for t in tasks]
     for (b, h), (o_bh, l_bh) in zip(todo, results):
@@ -285,7 +287,7 @@ def lse_merge(parts: List[Tuple[np.ndarray, np.ndarray]]) -> Tuple[np.ndarray, n
 
 
 def default_workers() -> int:
-    """Host cores available to this process (the oracle's process-pool width)."""
+    """Host cores available to this process (the oracle's worker-thread count)."""
     try:
         return max(1, len(os.sched_getaffinity(0)))
     except AttributeError:  # pragma: no cover

@@ -1,0 +1,138 @@
+"""The C-ABI library loads, exports what include/attn.h declares, and rejects
+bad arguments on the host before any HIP call (no GPU needed: every call here
+fails validation, so no kernel is ever launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_attention_04_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+FAKE = 0x10000  # a non-null, 16-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(bd.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(bd.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_error_strings():
+    for code in (0, -1, -2, -3, -4):
+        assert bd.attn_strerror(code) and "unknown" not in bd.attn_strerror(code)
+    assert "unknown" in bd.attn_strerror(7)
+
+
+def fwd_args(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=4, Hkv=2, Sq=16, Sk=16, d=128,
+             causal=1, scale=0.088, dtype=bd.ATTN_BF16, stream=None)
+    a.update(kw)
+    return a
+
+
+def call_fwd(**kw):
+    a = fwd_args(**kw)
+    return bd.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["Sq"], a["Sk"],
+                       a["d"], a["causal"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(k=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(v=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(o=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(q=FAKE + 8), bd.ATTN_ERR_INVALID_ARG),
+    (dict(o=FAKE + 2), bd.ATTN_ERR_INVALID_ARG),
+    (dict(lse=FAKE + 2), bd.ATTN_ERR_INVALID_ARG),
+    (dict(B=-1), bd.ATTN_ERR_INVALID_ARG),
+    (dict(Sq=-3), bd.ATTN_ERR_INVALID_ARG),
+    (dict(Sk=-1), bd.ATTN_ERR_INVALID_ARG),
+    (dict(H=0), bd.ATTN_ERR_INVALID_ARG),
+    (dict(Hkv=0), bd.ATTN_ERR_INVALID_ARG),
+    (dict(H=6, Hkv=4), bd.ATTN_ERR_INVALID_ARG),
+    (dict(scale=0.0), bd.ATTN_ERR_INVALID_ARG),
+    (dict(scale=-0.1), bd.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), bd.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), bd.ATTN_ERR_INVALID_ARG),
+    (dict(d=96), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(d=256), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=2), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(Sq=1 << 30, H=1 << 20, Hkv=1 << 20), bd.ATTN_ERR_INVALID_ARG),
+])
+def test_fwd_rejects(kw, code):
+    assert call_fwd(**kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(Sq=0), dict(B=0, q=None, o=None, k=None, v=None),
+                                dict(Sq=0, q=None, o=None)])
+def test_fwd_empty_is_a_noop(kw):
+    assert call_fwd(**kw) == bd.ATTN_OK
+
+
+def verify_args(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, sl=FAKE, maxs=3000, stride=3000, o=FAKE, lse=FAKE, B=2, H=32, Hkv=8,
+             kq=5, d=128, scale=0.088, dtype=bd.ATTN_BF16, ws=FAKE, wsb=None, stream=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = bd.attn_verify_workspace_bytes(a["B"], a["H"], a["kq"], 128, a["maxs"])
+    return a
+
+
+def call_verify(**kw):
+    a = verify_args(**kw)
+    return bd.attn_verify(a["q"], a["k"], a["v"], a["sl"], a["maxs"], a["stride"], a["o"], a["lse"], a["B"],
+                          a["H"], a["Hkv"], a["kq"], a["d"], a["scale"], a["dtype"], a["ws"], a["wsb"],
+                          a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(k=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(sl=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(sl=FAKE + 2), bd.ATTN_ERR_INVALID_ARG),
+    (dict(ws=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(ws=FAKE + 4), bd.ATTN_ERR_INVALID_ARG),
+    (dict(maxs=3001), bd.ATTN_ERR_INVALID_ARG),
+    (dict(maxs=-1), bd.ATTN_ERR_INVALID_ARG),
+    (dict(kq=0), bd.ATTN_ERR_INVALID_ARG),
+    (dict(H=30), bd.ATTN_ERR_INVALID_ARG),
+    (dict(scale=0.0), bd.ATTN_ERR_INVALID_ARG),
+    (dict(dtype=bd.ATTN_F32), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(d=80), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(kq=9), bd.ATTN_ERR_UNSUPPORTED),        # 4 heads * 9 tokens > 32 packed rows
+    (dict(H=64, Hkv=1, kq=1), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(wsb=100), bd.ATTN_ERR_WORKSPACE),
+])
+def test_verify_rejects(kw, code):
+    assert call_verify(**kw) == code
+
+
+def test_verify_workspace_formula():
+    # fp32 O and LSE partials for every (sequence, query head, token, chunk)
+    C = 1024
+    for B, H, kq, d, m in [(8, 32, 5, 128, 16025), (1, 8, 1, 64, 1), (2, 4, 3, 128, 1024), (2, 4, 3, 128, 1025)]:
+        nch = -(-m // C)
+        n = B * H * kq * nch
+        up = lambda x: -(-x // 256) * 256
+        assert bd.attn_verify_workspace_bytes(B, H, kq, d, m) == up(n * d * 4) + up(n * 4)
+    assert bd.attn_verify_workspace_bytes(1, 8, 5, 128, 0) == 0
+    assert bd.attn_verify_workspace_bytes(1, 8, 5, 96, 10) == 0
+    assert bd.attn_verify_workspace_bytes(-1, 8, 5, 128, 10) == 0
+
+
+def test_verify_empty_batch_is_a_noop():
+    assert call_verify(B=0, q=None, o=None, sl=None, k=None, v=None, ws=None, maxs=0, stride=0) == bd.ATTN_OK

@@ -1,0 +1,134 @@
+"""GPU parity of attn_fwd against the CPU fp64 oracle (through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_04_amd import synth
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    from exact_attention_04_amd import binding  # raises if the library is missing
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return binding
+
+
+# ------------------------------------------------------------------ named workloads, every output
+def test_noncausal_f32_s256_full():
+    w = synth.NONCAUSAL_F32_S256
+    q, k, v = synth.prefill_inputs(w, "cuda")
+    P.log(f"[fwd] {w.name}")
+    o, lse = P.run_fwd(q, k, v, w.causal, w.scale)
+    P.check_fwd(q, k, v, o, lse, w.causal, w.scale, "f32", what=w.name)
+
+
+@pytest.mark.parametrize("w", [synth.CAUSAL_BF16_S2048, synth.CAUSAL_BF16_S2048_Q8], ids=lambda w: w.name)
+def test_causal_bf16_s2048_full(w):
+    q, k, v = synth.prefill_inputs(w, "cuda")
+    P.log(f"[fwd] {w.name}")
+    o, lse = P.run_fwd(q, k, v, w.causal, w.scale)
+    res = P.check_fwd(q, k, v, o, lse, w.causal, w.scale, "bf16", what=w.name)
+    P.log(f"    max logit {float((synth.to_f64(q[0, 0]) @ synth.to_f64(k[0, 0]).T).max() * w.scale):.2f} {res}")
+
+
+def test_q_times_16_stress():
+    """Logits up to ~100 overflow fp32 exp without the max subtraction."""
+    P.fwd_case(16, 1, 4, 4, 1024, 1024, 128, True, "bf16", q_mult=16.0, what="qx16")
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled rows
+SAMPLE_ROWS = lambda S: sorted(set([0, 1, 2, 31, 32, 63, 64, 65, 127, 128, 129, 255, 256, 1000, S // 2 - 1, S // 2,
+                                    S - 129, S - 128, S - 65, S - 64, S - 2, S - 1]))
+
+
+@pytest.mark.parametrize("w", [synth.CAUSAL_BF16_S8192, synth.CAUSAL_BF16_S32768_D128,
+                               synth.CAUSAL_BF16_S32768_D64], ids=lambda w: w.name)
+def test_full_size_sampled(w):
+    q, k, v = synth.prefill_inputs(w, "cuda")
+    P.log(f"[fwd] {w.name} (sampled)")
+    o, lse = P.run_fwd(q, k, v, w.causal, w.scale)
+    heads = [(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 2 + 1)]
+    P.check_fwd(q, k, v, o, lse, w.causal, w.scale, "bf16", rows=SAMPLE_ROWS(w.Sq), heads=heads, what=w.name)
+    # properties at every row: finite, and |O| bounded by max |V| (convex combination)
+    o32 = o.float()
+    assert torch.isfinite(o32).all()
+    assert float(o32.abs().max()) <= float(v.float().abs().max()) + 2e-2
+    assert torch.isfinite(lse).all()
+
+
+# ------------------------------------------------------------------ ragged and edge shapes
+EDGE_S = [1, 2, 17, 63, 64, 65, 127, 129, 1000]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_square_edges(dtype, d, causal):
+    for S in EDGE_S:
+        P.fwd_case(S, 1, 2, 1, S, S, d, causal, dtype, what=f"square S={S}")
+
+
+@pytest.mark.parametrize("Sq,Sk", [(1, 300), (5, 1029), (17, 64), (200, 129), (300, 70), (129, 4097), (64, 1)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rectangular_bottom_right(Sq, Sk, causal, dtype):
+    P.fwd_case(Sq + Sk, 2, 4, 2, Sq, Sk, 128, causal, dtype, what="rect")
+
+
+@pytest.mark.parametrize("H,Hkv", [(8, 1), (8, 2), (8, 8)])
+def test_gqa_ratios(H, Hkv):
+    P.fwd_case(H * 10 + Hkv, 2, H, Hkv, 300, 300, 128, True, "bf16", what="gqa")
+
+
+def test_sk_zero_gives_empty_rows():
+    q, k, v = synth.random_qkv(1, 1, 2, 2, 40, 1, 128, "bf16", device="cuda")
+    k0, v0 = k[:, :, :0].contiguous(), v[:, :, :0].contiguous()
+    from exact_attention_04_amd import binding
+    o, lse = binding.fwd(q, k0, v0, causal=False)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+# ------------------------------------------------------------------ hygiene
+def test_repeat_is_bitwise_deterministic():
+    w = synth.CAUSAL_BF16_S2048
+    q, k, v = synth.prefill_inputs(w, "cuda")
+    o1, l1 = P.run_fwd(q, k, v, True, w.scale)
+    o2, l2 = P.run_fwd(q, k, v, True, w.scale)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_guard_bands_untouched_and_tail_not_read():
+    """O/LSE live inside larger buffers whose guard bands must stay as filled;
+    K/V are followed by NaN, so an over-read past the last key would poison O."""
+    from exact_attention_04_amd import binding
+    B, H, Hkv, Sq, Sk, d = 1, 4, 2, 190, 190, 128
+    q, k, v = synth.random_qkv(5, B, H, Hkv, Sq, Sk, d, "bf16", device="cuda")
+    g = 4096
+    kbuf = torch.full((k.numel() + g,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vbuf = torch.full((v.numel() + g,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    kbuf[:k.numel()] = k.reshape(-1)
+    vbuf[:v.numel()] = v.reshape(-1)
+    kk, vv = kbuf[:k.numel()].view(k.shape), vbuf[:v.numel()].view(v.shape)
+    obuf = torch.full((q.numel() + 2 * g,), 7.0, dtype=torch.bfloat16, device="cuda")
+    lbuf = torch.full((B * H * Sq + 2 * g,), 7.0, dtype=torch.float32, device="cuda")
+    o = obuf[g:g + q.numel()].view(q.shape)
+    lse = lbuf[g:g + B * H * Sq].view(B, H, Sq)
+    for causal in (False, True):
+        binding.fwd(q, kk, vv, causal=causal, scale=float(np.float32(d ** -0.5)), out=o, lse=lse)
+        torch.cuda.synchronize()
+        assert torch.all(obuf[:g] == 7.0) and torch.all(obuf[g + q.numel():] == 7.0)
+        assert torch.all(lbuf[:g] == 7.0) and torch.all(lbuf[g + B * H * Sq:] == 7.0)
+        P.check_fwd(q, k, v, o, lse, causal, float(np.float32(d ** -0.5)), "bf16", what="guard")
+
+
+def test_lse_optional():
+    from exact_attention_04_amd import binding
+    q, k, v = synth.random_qkv(9, 1, 2, 2, 100, 100, 64, "bf16", device="cuda")
+    o1, _ = binding.fwd(q, k, v, causal=True, want_lse=False)
+    o2, _ = binding.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)

@@ -1,0 +1,107 @@
+"""GPU parity of attn_verify (split-KV + merge) against the CPU fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_04_amd import synth
+from oracle import ref_attention as ref
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    from exact_attention_04_amd import binding
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return binding
+
+
+def poison_tail(k, v, seqlens):
+    """Cache rows at or beyond seqlens[b] become NaN: any over-read shows up."""
+    for b, s in enumerate(seqlens.tolist()):
+        k[b, :, max(s, 0):] = float("nan")
+        v[b, :, max(s, 0):] = float("nan")
+
+
+def run_verify(q, k, v, sl, max_len, scale):
+    from exact_attention_04_amd import binding
+    o, lse = binding.verify(q, k, v, sl, max_len, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check_verify(q, k, v, sl_host, o, lse, scale, what):
+    qn, kn, vn = synth.to_f64(q), synth.to_f64(k), synth.to_f64(v)
+    kn = np.nan_to_num(kn, nan=0.0)  # the oracle never reads past seqlens either
+    vn = np.nan_to_num(vn, nan=0.0)
+    o_ref, l_ref = ref.verify(qn, kn, vn, sl_host, scale)
+    res = P.compare(synth.to_f64(o), synth.to_f64(lse), o_ref, l_ref, "bf16", what)
+    P.log(f"    ok {res}")
+    return res
+
+
+def verify_case(seed, lengths, H, Hkv, kq, d, what=""):
+    """lengths = total keys per sequence (including the kq new ones)."""
+    B = len(lengths)
+    rng = np.random.default_rng(seed)
+    sl = np.asarray(lengths, dtype=np.int32)
+    stride = max(1, int(sl.max()) + 3)
+    q = synth.normal(rng, (B, H, kq, d), "bf16").cuda()
+    k = synth.normal(rng, (B, Hkv, stride, d), "bf16").cuda()
+    v = synth.normal(rng, (B, Hkv, stride, d), "bf16").cuda()
+    poison_tail(k, v, torch.from_numpy(sl))
+    slt = torch.from_numpy(sl).cuda()
+    scale = float(np.float32(d ** -0.5))
+    P.log(f"[verify] {what} seed={seed} lengths={lengths} H={H} Hkv={Hkv} kq={kq} d={d}")
+    o, lse = run_verify(q, k, v, slt, int(sl.max()), scale)
+    return check_verify(q, k, v, sl, o, lse, scale, what)
+
+
+def test_verify_workload_full():
+    w = synth.VERIFY_BF16
+    q, k, v, sl = synth.verify_inputs(w, "cuda")
+    poison_tail(k, v, sl)
+    P.log(f"[verify] {w.name} lengths={sl.tolist()}")
+    o, lse = run_verify(q, k, v, sl, int(sl.max()), w.scale)
+    check_verify(q, k, v, sl.cpu().numpy(), o, lse, w.scale, w.name)
+
+
+@pytest.mark.parametrize("kq", [1, 5, 6])
+def test_chunk_boundaries(kq):
+    C = 1024
+    lengths = [C - 1, C, C + 1, 2 * C, 2 * C + kq, kq, 1, 3 * C - 2]
+    verify_case(kq, lengths, 32, 8, kq, 128, what="chunk-boundaries")
+
+
+def test_fewer_keys_than_queries_and_empty():
+    verify_case(11, [0, 1, 2, 4, 5, 6], 8, 2, 5, 128, what="short")
+
+
+@pytest.mark.parametrize("H,Hkv,kq", [(8, 8, 5), (16, 2, 4), (32, 4, 4), (4, 1, 8), (32, 1, 1)])
+def test_gqa_packing(H, Hkv, kq):
+    verify_case(H + Hkv + kq, [700, 3000, 5], H, Hkv, kq, 128, what="gqa")
+
+
+def test_head_dim_64():
+    verify_case(64, [2500, 17, 1024], 16, 4, 5, 64, what="d64")
+
+
+def test_device_lengths_clamped_to_max():
+    """Device lengths above max_seqlen_k are clamped to it (documented)."""
+    rng = np.random.default_rng(3)
+    B, H, Hkv, kq, d, stride = 2, 8, 2, 5, 128, 1500
+    q = synth.normal(rng, (B, H, kq, d), "bf16").cuda()
+    k = synth.normal(rng, (B, Hkv, stride, d), "bf16").cuda()
+    v = synth.normal(rng, (B, Hkv, stride, d), "bf16").cuda()
+    sl = torch.tensor([1400, 9999], dtype=torch.int32, device="cuda")
+    o, lse = run_verify(q, k, v, sl, 1200, float(np.float32(d ** -0.5)))
+    check_verify(q, k, v, np.array([1200, 1200]), o, lse, float(np.float32(d ** -0.5)), "clamp")
+
+
+def test_verify_deterministic():
+    w = synth.VERIFY_BF16
+    q, k, v, sl = synth.verify_inputs(w, "cuda")
+    o1, l1 = run_verify(q, k, v, sl, int(sl.max()), w.scale)
+    o2, l2 = run_verify(q, k, v, sl, int(sl.max()), w.scale)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

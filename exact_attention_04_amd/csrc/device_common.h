@@ -45,6 +45,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// c + lo + hi of a packed bf16 pair, exact products, fp32 accumulation
+// (v_dot2_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float sum_bf16x2(uint32_t packed, float c) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, c, false);
+}
+
 // Low 16-bit halves of a and b packed as (a.lo, b.lo); high halves likewise.
 __device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x05040100u);

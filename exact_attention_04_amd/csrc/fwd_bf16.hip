@@ -10,20 +10,30 @@
 //
 // Mapping onto CDNA4:
 //   * one workgroup = 4 waves = 128 query rows of one (batch, head); each wave
-//     owns 32 rows; K/V tiles of 64 keys are staged in LDS and shared by the
-//     four waves;
-//   * scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16
-//     MFMA, so that each lane holds one query column and 32 of the tile's 64
-//     keys: the row max is an in-lane reduction plus one exchange with the
-//     other wave half, and the row sum is kept per lane until the end;
+//     owns 32 rows; K/V tiles of 64 keys are shared by the four waves through
+//     LDS, double-buffered and filled by direct HBM->LDS loads
+//     (global_load_lds_dwordx4), so the next tile streams in while the
+//     current one is consumed and no registers hold staged data;
+//   * scores are computed transposed, S^T = K Q^T, on the 32x32x16 bf16 MFMA,
+//     so each lane holds one query column and 32 of the tile's 64 keys: the
+//     row max is an in-lane reduction plus one exchange with the other wave
+//     half, and the row sum stays per lane until the end;
 //   * the output is accumulated transposed too, O^T += V^T P^T: P^T is the
-//     B operand straight from the score registers (rounded to bf16), and the
-//     rescale factor of a query is a per-lane scalar;
-//   * V^T operands are built from row-major V in LDS: lane m reads, for each
-//     of its 8 keys, the head-dim elements [NDB*m, NDB*m + NDB) and
-//     regroups them with byte permutes, so O^T row m of d-block db holds head
-//     dim NDB*m + db;
+//     B operand straight from the score registers (rounded to bf16), the V^T
+//     A operand comes from row-major V with the LDS transpose read
+//     (ds_read_b64_tr_b16), and the rescale factor of a query is a per-lane
+//     scalar;
 //   * the softmax works in base 2 with scale*log2(e) folded into one FMA.
+//     The reference max of a row is only raised when the tile max exceeds it
+//     by more than 2^8 (the exponents then stay <= 8, far from overflow); the
+//     final O/l and LSE are unchanged by the choice of reference, as in Ch.3's
+//     rescaling identity, and most tiles skip the accumulator rescale;
+//   * two denominators are kept: the fp32 sum of the probabilities (for LSE)
+//     and the sum of the same probabilities rounded to bf16, i.e. of exactly
+//     the weights the P.V product used (one v_dot2 per pair).  O is divided by
+//     the latter, so O is a convex combination of V rows whose weights sum to
+//     one; the bf16 rounding of a dominant weight then cancels instead of
+//     showing up as an error of |v| * 2^-9.
 #include "device_common.h"
 #include "launch.h"
 
@@ -34,6 +44,12 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBr = 32 * kWaves;  // query rows per workgroup
 constexpr int kBc = 64;           // keys per K/V tile
+constexpr float kRescaleSlack = 8.0f;  // log2 units
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 struct FwdKernelArgs {
   const uint16_t* q;
@@ -42,19 +58,36 @@ struct FwdKernelArgs {
   uint16_t* o;
   float* lse;
   int H, Hkv, Sq, Sk;
-  int nqb;        // query blocks per (batch, head)
-  float c2;       // scale * log2(e)
+  int nqb;   // query blocks per (batch, head)
+  float c2;  // scale * log2(e)
 };
+
+// 16-byte chunk positions inside an LDS row (XOR swizzles).  K: the 32 rows
+// an A-operand read touches spread over all banks.  V: the 8 rows x 64 bytes
+// a transpose read touches spread over all banks.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) { return row & (D / 8 - 1); }
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+  return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+}
+
+__device__ __forceinline__ void wait_vmem_all() {
+  // s_waitcnt vmcnt(0), other counters untouched
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(FwdKernelArgs a) {
   constexpr int CPR = D / 8;   // 16-byte chunks per K/V row
   constexpr int KS = D / 16;   // MFMA steps over the head dim for S^T
   constexpr int NDB = D / 32;  // 32-row blocks of O^T (head dim)
-  constexpr int CPT = kBc * CPR / kThreads;  // staged chunks per thread per tile
+  constexpr int TILE = kBc * D;  // elements per K or V tile
+  constexpr int ROWS_PER_INSN = 1024 / (D * 2);  // rows one wave-wide 1 KB load covers
+  constexpr int INSN_PER_WAVE = TILE * 2 / 1024 / kWaves;
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kBc * D];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kBc * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2][TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -84,6 +117,27 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(FwdKernelArgs a) 
   kend = max(kend, 0);
   const int nkt = (kend + kBc - 1) / kBc;
 
+  // ---- direct HBM -> LDS tile loads.  Wave-wide instruction i of this wave
+  // fills LDS bytes [1024*(wave*INSN_PER_WAVE + i), +1024); lane l's 16
+  // bytes land at offset 16*l, i.e. row r = first row + l / CPR, chunk
+  // position l % CPR, which holds global chunk (position ^ swizzle(r)).
+  // Rows past Sk re-read row Sk-1: finite data whose probability is 0.
+  auto issue_tile = [&](int j0, int buf) {
+#pragma unroll
+    for (int i = 0; i < INSN_PER_WAVE; ++i) {
+      const int insn = wave * INSN_PER_WAVE + i;
+      const int row = insn * ROWS_PER_INSN + lane / CPR;
+      const int pos = lane % CPR;
+      const int grow = min(j0 + row, a.Sk - 1);
+      const uint16_t* kg = K + (size_t)grow * D + ((pos ^ k_swz<D>(row)) * 8);
+      const uint16_t* vg = V + (size_t)grow * D + ((pos ^ v_swz<D>(row)) * 8);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)kg,
+                                       (lds_void*)(&k_lds[buf][insn * 512]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)vg,
+                                       (lds_void*)(&v_lds[buf][insn * 512]), 16, 0, 0);
+    }
+  };
+
   // Q^T as the B operand: column n = query, eight head-dim values per step.
   u32x4 qf[KS];
 #pragma unroll
@@ -94,165 +148,145 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(FwdKernelArgs a) 
   f32x16 acc_o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
-  float m_run = -INFINITY;  // running max, base-2 domain (scaled logits * log2 e)
+  float m_ref = -INFINITY;  // reference max, base-2 domain (scaled logits * log2 e)
   float l_run = 0.f;        // running denominator, this lane's keys only
+  float l_rnd = 0.f;        // same, of the bf16-rounded probabilities
 
-  u32x4 kst[CPT], vst[CPT];
-  auto stage = [&](int j0) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ci = tid + i * kThreads;
-      const int row = ci / CPR, c = ci % CPR;
-      const bool ok = j0 + row < a.Sk;
-      const size_t off = (size_t)(j0 + row) * D + c * 8;
-      kst[i] = ok ? load16(K + off) : u32x4{0, 0, 0, 0};
-      vst[i] = ok ? load16(V + off) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto commit = [&]() {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ci = tid + i * kThreads;
-      const int row = ci / CPR, c = ci % CPR;
-      // K rows are XOR-swizzled in 16-byte chunks so that the 32 different
-      // rows an MFMA A-operand read touches fall in distinct banks.
-      store16(&k_lds[row * D + ((c ^ (row & (CPR - 1))) * 8)], kst[i]);
-      store16(&v_lds[row * D + c * 8], vst[i]);
-    }
-  };
+  // lane constants of the transpose read: group of 16 lanes gq, row r4 of
+  // the 4x16 block this lane addresses, 4-element column chunk c4
+  const int gq = lane >> 4, r4 = (lane >> 2) & 3, c4 = lane & 3;
 
-  if (nkt > 0) {
-    stage(0);
-    commit();
-  }
-  __syncthreads();
-
-  for (int jt = 0; jt < nkt; ++jt) {
-    const int j0 = jt * kBc;
-    if (jt + 1 < nkt) stage(j0 + kBc);  // global loads overlap this tile's math
-
+  auto compute_tile = [&](int j0, int buf) {
     const bool wave_live = (wq0 < a.Sq) && (!CAUSAL || j0 <= wq0 + 31 + shift);
-    if (wave_live) {
-      // ---- S^T = K Q^T for the two 32-key blocks of the tile
-      f32x16 s[2];
+    if (!wave_live) return;
+    const lds_u16* kt = (const lds_u16*)&k_lds[buf][0];
+    const lds_u16* vt = (const lds_u16*)&v_lds[buf][0];
+    // ---- S^T = K Q^T for the two 32-key blocks of the tile
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
         const int krow = kb * 32 + n;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int c = (ks * 2 + h) ^ (krow & (CPR - 1));
-          const u32x4 kf = *reinterpret_cast<const u32x4*>(&k_lds[krow * D + c * 8]);
-          s[kb] = mfma_32x32x16_bf16(kf, qf[ks], s[kb]);
-        }
+        const int c = (ks * 2 + h) ^ k_swz<D>(krow);
+        const u32x4 kf = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(kt + krow * D + c * 8);
+        s[kb] = mfma_32x32x16_bf16(kf, qf[ks], s[kb]);
       }
-      // ---- mask the causal diagonal and the ragged tail (only where needed)
-      const bool need_mask = (j0 + kBc > a.Sk) || (CAUSAL && j0 + kBc - 1 > wq0 + shift);
-      if (need_mask) {
-        const int lim = CAUSAL ? min(a.Sk - 1, qrow + shift) : a.Sk - 1;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j0 + kb * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-            if (key > lim) s[kb][r] = -INFINITY;
-          }
-      }
-      // ---- online softmax (base 2)
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, swap_halves(mx));
-      const float m_new = fmaxf(m_run, mx * a.c2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // all-masked so far
-      const float alpha = fast_exp2(m_run - m_use);
-      float rs = 0.f;
+    }
+    // ---- mask the causal diagonal and the ragged tail (only where needed)
+    const bool need_mask = (j0 + kBc > a.Sk) || (CAUSAL && j0 + kBc - 1 > wq0 + shift);
+    if (need_mask) {
+      const int lim = CAUSAL ? min(a.Sk - 1, qrow + shift) : a.Sk - 1;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(s[kb][r], a.c2, -m_use));
-          s[kb][r] = p;
-          rs += p;
+          const int key = j0 + kb * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+          if (key > lim) s[kb][r] = -INFINITY;
         }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-      if (__any(alpha != 1.f)) {
+    }
+    // ---- online softmax (base 2, lazily raised reference max)
+    float mx = -INFINITY;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, swap_halves(mx)) * a.c2;
+    const bool raise = mx > m_ref + kRescaleSlack;
+    if (__any(raise)) {
+      const float m_new = raise ? mx : m_ref;
+      const float alpha = raise ? fast_exp2(m_ref - mx) : 1.f;  // 0 when m_ref = -inf
+      l_run *= alpha;
+      l_rnd *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+      m_ref = m_new;
+    }
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;  // nothing visible yet
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(s[kb][r], a.c2, -m_use));
+        s[kb][r] = p;
+        rs += p;
       }
-      // ---- O^T += V^T P^T over four 16-key steps
+    l_run += rs;
+    // ---- O^T += V^T P^T over four 16-key steps
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int kb = t >> 1, base = (t & 1) * 8;
-        u32x4 pt;
-        pt[0] = pack_bf16x2(s[kb][base + 0], s[kb][base + 1]);
-        pt[1] = pack_bf16x2(s[kb][base + 2], s[kb][base + 3]);
-        pt[2] = pack_bf16x2(s[kb][base + 4], s[kb][base + 5]);
-        pt[3] = pack_bf16x2(s[kb][base + 6], s[kb][base + 7]);
-        // the 8 keys of this step held by this lane half (same order as pt)
-        uint32_t x[8][NDB / 2];
+    for (int t = 0; t < 4; ++t) {
+      const int kb = t >> 1, base = (t & 1) * 8;
+      u32x4 pt;
+      pt[0] = pack_bf16x2(s[kb][base + 0], s[kb][base + 1]);
+      pt[1] = pack_bf16x2(s[kb][base + 2], s[kb][base + 3]);
+      pt[2] = pack_bf16x2(s[kb][base + 4], s[kb][base + 5]);
+      pt[3] = pack_bf16x2(s[kb][base + 6], s[kb][base + 7]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int key = 16 * t + 8 * (e / 4) + 4 * h + (e % 4);
-          const uint16_t* src = &v_lds[key * D + NDB * n];
-          if constexpr (NDB == 4) {
-            const u32x2 w = *reinterpret_cast<const u32x2*>(src);
-            x[e][0] = w[0];
-            x[e][1] = w[1];
-          } else {
-            x[e][0] = *reinterpret_cast<const uint32_t*>(src);
-          }
+      for (int w = 0; w < 4; ++w) l_rnd = sum_bf16x2(pt[w], l_rnd);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        // items 0..3: keys 16t + 4h + r4; items 4..7: keys 16t + 8 + 4h + r4
+        // column chunk: head dims 32*db + 16*(gq & 1) + 4*c4 .. +3
+        const int dcol = 32 * db + 16 * (gq & 1) + 4 * c4;
+        i16x4 lo, hi;
+        {
+          const int row = 16 * t + 4 * h + r4;
+          const int pos = (dcol >> 3) ^ v_swz<D>(row);
+          lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + row * D + pos * 8 + (dcol & 7)));
         }
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          u32x4 vf;
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const uint32_t lo = x[2 * e2][db / 2], hi = x[2 * e2 + 1][db / 2];
-            vf[e2] = (db & 1) ? pack_hi16(lo, hi) : pack_lo16(lo, hi);
-          }
-          acc_o[db] = mfma_32x32x16_bf16(vf, pt, acc_o[db]);
+        {
+          const int row = 16 * t + 8 + 4 * h + r4;
+          const int pos = (dcol >> 3) ^ v_swz<D>(row);
+          hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + row * D + pos * 8 + (dcol & 7)));
         }
+        u32x4 vf;
+        vf[0] = __builtin_bit_cast(u32x2, lo)[0];
+        vf[1] = __builtin_bit_cast(u32x2, lo)[1];
+        vf[2] = __builtin_bit_cast(u32x2, hi)[0];
+        vf[3] = __builtin_bit_cast(u32x2, hi)[1];
+        acc_o[db] = mfma_32x32x16_bf16(vf, pt, acc_o[db]);
       }
     }
+  };
+
+  if (nkt > 0) issue_tile(0, 0);
+  wait_vmem_all();
+  __syncthreads();
+  for (int jt = 0; jt < nkt; jt += 2) {
+    // even tile from buffer 0, odd tile from buffer 1 (static buffer index)
+    if (jt + 1 < nkt) issue_tile((jt + 1) * kBc, 1);
+    compute_tile(jt * kBc, 0);
+    wait_vmem_all();
     __syncthreads();
     if (jt + 1 < nkt) {
-      commit();
+      if (jt + 2 < nkt) issue_tile((jt + 2) * kBc, 0);
+      compute_tile((jt + 1) * kBc, 1);
+      wait_vmem_all();
       __syncthreads();
     }
   }
 
   // ---- epilogue: one normalised write per row
   const float lt = l_run + swap_halves(l_run);
+  const float lr = l_rnd + swap_halves(l_rnd);
   if (qrow < a.Sq) {
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float inv = lr > 0.f ? 1.f / lr : 0.f;
     uint16_t* O = a.o + ((size_t)(b * a.H + hq) * a.Sq + qrow) * D;
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      // registers 4*rg .. 4*rg+3 of every d-block: head dims
-      // [NDB*(8*rg + 4*h), NDB*(8*rg + 4*h) + 4*NDB) contiguous
-      uint32_t w[2 * NDB];
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int ri = 0; ri < 4; ++ri) {
-#pragma unroll
-        for (int db = 0; db < NDB; db += 2) {
-          w[(ri * NDB + db) / 2] = pack_bf16x2(acc_o[db][4 * rg + ri] * inv, acc_o[db + 1][4 * rg + ri] * inv);
-        }
+      for (int rg = 0; rg < 4; ++rg) {
+        // registers 4*rg .. 4*rg+3: head dims 32*db + 8*rg + 4*h + 0..3
+        const uint32_t w0 = pack_bf16x2(acc_o[db][4 * rg + 0] * inv, acc_o[db][4 * rg + 1] * inv);
+        const uint32_t w1 = pack_bf16x2(acc_o[db][4 * rg + 2] * inv, acc_o[db][4 * rg + 3] * inv);
+        *reinterpret_cast<u32x2*>(O + 32 * db + 8 * rg + 4 * h) = u32x2{w0, w1};
       }
-      uint16_t* dst = O + NDB * (8 * rg + 4 * h);
-#pragma unroll
-      for (int c = 0; c < NDB / 2; ++c) {
-        store16(dst + c * 8, u32x4{w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]});
-      }
-    }
     if (a.lse != nullptr && h == 0) {
       a.lse[(size_t)(b * a.H + hq) * a.Sq + qrow] =
-          lt > 0.f ? (m_run + fast_log2(lt)) * kLn2 : -INFINITY;
+          lt > 0.f ? (m_ref + fast_log2(lt)) * kLn2 : -INFINITY;
     }
   }
 }

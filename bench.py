@@ -69,12 +69,43 @@ def cpu_baseline(w, max_seconds_hint: float = 20.0) -> dict:
                       f"fp64 materialised rows; {dt:.1f} s wall; causal FLOPs halved like the GPU figure"}
 
 
+def profile_leg(args, dev) -> int:
+    """Run one leg warmup+steps times with no timing or output (for rocprofv3)."""
+    import torch
+    from exact_attention_04_amd import binding, synth
+
+    n = args.warmup + args.steps
+    if args.only == "copy":
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(n):
+            dst.copy_(src)
+    elif args.only == "prefill":
+        w = synth.CAUSAL_BF16_S8192
+        q, k, v = synth.prefill_inputs(w, dev)
+        for _ in range(n):
+            binding.fwd(q, k, v, causal=True, scale=w.scale)
+    else:
+        w = synth.VERIFY_BF16
+        q, kc, vc, sl = synth.verify_inputs(w, dev)
+        caches = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(3)]
+        m = int(sl.max())
+        for i in range(n):
+            binding.verify(q, caches[i % 4][0], caches[i % 4][1], sl, m, scale=w.scale)
+    torch.cuda.synchronize()
+    log(f"profile leg {args.only}: {n} calls done")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "verify", "copy"], default=None,
+                    help="profiling aid: run just one leg (no JSON line); 'copy' runs a plain "
+                         "1 GiB device-to-device copy used to calibrate the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the attention path "
@@ -86,6 +117,8 @@ def main() -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.only is not None:
+        return profile_leg(args, dev)
     props = torch.cuda.get_device_properties(dev)
     wp = synth.CAUSAL_BF16_S8192
     wv = synth.VERIFY_BF16

@@ -66,6 +66,10 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// max / sum of x over lanes l and l ^ 32.
+__device__ __forceinline__ float max_halves(float x) { return fmaxf(x, swap_halves(x)); }
+__device__ __forceinline__ float sum_halves(float x) { return x + swap_halves(x); }
+
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

@@ -134,7 +134,7 @@ def main() -> int:
     caches = [(vk, vv)] + [(vk.clone(), vv.clone()) for _ in range(n_rot - 1)]
     vo = torch.empty_like(vq)
     vlse = torch.empty((wv.B, wv.H, wv.kq), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(16, binding.attn_verify_workspace_bytes(wv.B, wv.H, wv.kq, wv.d, max_len)),
+    ws = torch.empty(max(16, binding.attn_verify_workspace_bytes(wv.B, wv.H, wv.Hkv, wv.kq, wv.d)),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 

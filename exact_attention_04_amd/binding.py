@@ -37,7 +37,7 @@ _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_
 lib.attn_fwd.restype = _i
 lib.attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp]
 lib.attn_verify_workspace_bytes.restype = _sz
-lib.attn_verify_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
+lib.attn_verify_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]  # B, H, Hkv, kq, d
 lib.attn_verify.restype = _i
 lib.attn_verify.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]
 lib.attn_strerror.restype = ctypes.c_char_p
@@ -61,8 +61,8 @@ def attn_fwd(q, k, v, o, lse, B, H, Hkv, Sq, Sk, d, causal, scale, dtype, stream
     return lib.attn_fwd(q, k, v, o, lse, B, H, Hkv, Sq, Sk, d, int(causal), float(scale), dtype, stream)
 
 
-def attn_verify_workspace_bytes(B, H, kq, d, max_seqlen_k) -> int:
-    return int(lib.attn_verify_workspace_bytes(B, H, kq, d, max_seqlen_k))
+def attn_verify_workspace_bytes(B, H, Hkv, kq, d) -> int:
+    return int(lib.attn_verify_workspace_bytes(B, H, Hkv, kq, d))
 
 
 def attn_verify(q, k_cache, v_cache, seqlens_k, max_seqlen_k, cache_stride, o, lse, B, H, Hkv, kq, d,
@@ -126,7 +126,7 @@ def verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seqlen
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, H, kq), dtype=torch.float32, device=q.device)
-    need = attn_verify_workspace_bytes(B, H, kq, d, max_seqlen_k)
+    need = attn_verify_workspace_bytes(B, H, Hkv, kq, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if seqlens_k.dtype != torch.int32:

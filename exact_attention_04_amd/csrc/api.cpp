@@ -56,9 +56,9 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
-extern "C" size_t attn_verify_workspace_bytes(int B, int H, int kq, int d, int max_seqlen_k) {
-  if (B < 0 || H < 1 || kq < 1 || (d != 64 && d != 128) || max_seqlen_k < 0) return 0;
-  return attn::verify_workspace_bytes(B, H, kq, d, max_seqlen_k);
+extern "C" size_t attn_verify_workspace_bytes(int B, int H, int Hkv, int kq, int d) {
+  if (B < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || kq < 1 || (d != 64 && d != 128)) return 0;
+  return attn::verify_workspace_bytes(B, H, Hkv, kq, d);
 }
 
 extern "C" int attn_verify(const void* q, const void* k_cache, const void* v_cache,
@@ -72,6 +72,7 @@ extern "C" int attn_verify(const void* q, const void* k_cache, const void* v_cac
   if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   if ((H / Hkv) * kq > 32) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)B * max_seqlen_k >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;  // total keys fit int32
   const size_t nq = (size_t)B * H * kq * d;
   const size_t nk = (size_t)B * Hkv * cache_stride * d;
   if (nq > kMaxElems || nk > kMaxElems) return ATTN_ERR_INVALID_ARG;
@@ -79,7 +80,7 @@ extern "C" int attn_verify(const void* q, const void* k_cache, const void* v_cac
     return ATTN_ERR_INVALID_ARG;
   if (B > 0 && (seqlens_k == nullptr || !aligned4(seqlens_k))) return ATTN_ERR_INVALID_ARG;
   if (lse != nullptr && !aligned4(lse)) return ATTN_ERR_INVALID_ARG;
-  const size_t need = attn::verify_workspace_bytes(B, H, kq, d, max_seqlen_k);
+  const size_t need = attn::verify_workspace_bytes(B, H, Hkv, kq, d);
   if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (need > 0 && (workspace == nullptr || !aligned16(workspace))) return ATTN_ERR_INVALID_ARG;
   if (nq == 0) return ATTN_OK;

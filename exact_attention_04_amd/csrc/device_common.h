@@ -77,6 +77,44 @@ __device__ __forceinline__ void store16(void* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer descriptor flags (gfx9 family)
+
+// 16-byte chunk positions inside an LDS row (XOR swizzles).  K: the 32 rows
+// an A-operand read touches spread over all banks.  V: the 8 rows x 64 bytes
+// a transpose read touches spread over all banks.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) { return row & (D / 8 - 1); }
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+  return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+}
+
+// 16 bytes per lane from a raw buffer straight into LDS: lane l writes
+// lds_wave_base + 16*l (buffer_load_dwordx4 ... lds).  Out-of-range offsets
+// read as zero.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, uint16_t* lds_wave_base,
+                                                  uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 16, voffset, 0, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem_all() {
+  // s_waitcnt vmcnt(0), other counters untouched
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// s_waitcnt vmcnt(N): at most N of this wave's vector-memory operations
+// (including HBM->LDS loads) still outstanding; other counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vmem_at_most() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 // Workgroup index remapped so that the workgroups the hardware sends to one
 // XCD (dispatch is round-robin over the 8 XCDs) get consecutive logical ids:
 // neighbouring tiles of one head then share that XCD's L2.

@@ -66,12 +66,6 @@ constexpr int kBc = ATTN_FWD_BC;  // keys per K/V tile
 constexpr int kNkb = kBc / 32;    // 32-key blocks per tile
 constexpr int kMinBlocks = (kQb == 1 ? 8 : 4) / kWaves;  // waves per SIMD: 2 (one query block) or 1
 constexpr float kRescaleSlack = 8.0f;  // log2 units
-constexpr int kBufferWord3 = 0x00020000;  // raw buffer descriptor flags (gfx9 family)
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) uint16_t lds_u16;
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 struct FwdKernelArgs {
   const uint16_t* q;
@@ -84,34 +78,11 @@ struct FwdKernelArgs {
   float c2;  // scale * log2(e)
 };
 
-// 16-byte chunk positions inside an LDS row (XOR swizzles).  K: the 32 rows
-// an A-operand read touches spread over all banks.  V: the 8 rows x 64 bytes
-// a transpose read touches spread over all banks.
-template <int D>
-__device__ __forceinline__ int k_swz(int row) { return row & (D / 8 - 1); }
-template <int D>
-__device__ __forceinline__ int v_swz(int row) {
-  return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
-}
-
-// 16 bytes per lane from a raw buffer straight into LDS: lane l writes
-// lds_wave_base + 16*l (buffer_load_dwordx4 ... lds).  Out-of-range offsets
-// read as zero.
-__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, uint16_t* lds_wave_base,
-                                                  uint32_t voffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 16, voffset, 0, 0, 0);
-}
-
 __device__ __forceinline__ void prio_high() {
   if (ATTN_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
 }
 __device__ __forceinline__ void prio_low() {
   if (ATTN_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
-}
-
-__device__ __forceinline__ void wait_vmem_all() {
-  // s_waitcnt vmcnt(0), other counters untouched
-  __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
 template <int D, bool CAUSAL>

@@ -36,8 +36,8 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_verify_bf16(const VerifyArgs& a, hipStream_t s);
 
-// Keys per split-KV chunk of the verify path and the workspace it implies.
-int verify_chunk_keys();
-size_t verify_workspace_bytes(int B, int H, int kq, int d, int max_seqlen_k);
+// Workgroups of the verify split kernel and the workspace it needs.
+int verify_split_workgroups();
+size_t verify_workspace_bytes(int B, int H, int Hkv, int kq, int d);
 
 }  // namespace attn

@@ -8,207 +8,367 @@
 // "Warmup Guide -- Inference Optimization at Depth", Ch.3 written with
 // LSE = m + ln l.
 //
-// Split kernel -- one workgroup per (sequence b, KV head g, chunk of kChunk
-// keys):
+// Split kernel -- a fixed grid of kSplitWgs workgroups (one per CU on
+// MI355X).  The keys of all (sequence b, KV head g) segments, laid end to
+// end, are cut into kSplitWgs equal slices; a workgroup processes its slice,
+// i.e. the pieces of the one or few segments that overlap it, and writes one
+// partial per piece.  Every CU thus streams the same number of K/V bytes
+// whatever the length mix of the batch.  Per piece:
 //   * the (H/Hkv)*kq query rows that read KV head g are packed into one
-//     32-row tile, so each K/V byte of the chunk is read from HBM once;
-//   * the four waves take interleaved 32-key steps of the chunk; K and V go
-//     straight from HBM into matrix-core operands (each element is used by
-//     one wave only, so LDS staging would buy nothing);
+//     32-row tile, so each K/V byte is read from HBM once;
+//   * the four waves take interleaved 32-key steps of the piece.  Each wave
+//     streams its own steps HBM -> LDS with coalesced 16-byte
+//     buffer_load ... lds (one step ahead, two LDS stages per wave), so no
+//     wave ever waits for another and a CU keeps 64 KB of loads in flight;
 //   * S^T = K Q^T and O^T += V^T P^T on the 32x32x16 bf16 MFMA as in the
-//     prefill kernel; V^T operands come from 8-byte row segments regrouped
-//     with byte permutes;
-//   * the waves' (m, l, O) are combined through LDS and the chunk writes one
-//     fp32 partial (O_c normalised, base-2 LSE_c) per packed row.
-// Merge kernel -- one wave per output row combines the partials of its
-// sequence's chunks and writes O (bf16) and LSE (natural log).
+//     prefill kernel (K as 16-byte LDS reads, V^T via transpose reads), with
+//     the same base-2 online softmax, lazily raised reference max and the
+//     two denominators (fp32 for LSE, bf16-rounded for O);
+//   * the waves' (m, l, O) are combined through LDS into one fp32 partial
+//     (O normalised, base-2 LSE) per packed row.
+// Merge kernel -- one wave per output row combines its segment's piece
+// partials (weights exp(LSE_p - LSE)) and writes O (bf16) and LSE (natural
+// log).
 #include "device_common.h"
 #include "launch.h"
 
 namespace attn {
 namespace {
 
-constexpr int kChunk = 1024;  // keys per split-KV chunk
-constexpr int kWaves = 4;
+#ifndef ATTN_VERIFY_WAVES
+#define ATTN_VERIFY_WAVES 4
+#endif
+#ifndef ATTN_VERIFY_WGS
+#define ATTN_VERIFY_WGS 256
+#endif
+constexpr int kSplitWgs = ATTN_VERIFY_WGS;  // slices of the key range (one workgroup each)
+constexpr int kWaves = ATTN_VERIFY_WAVES;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStep = 32;  // keys per wave step
+constexpr float kRescaleSlack = 8.0f;  // log2 units
 
 struct SplitArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
   const int32_t* seqlens;
-  float* part_o;    // [B][Hkv][nch][R][D]
-  float* part_lse;  // [B][Hkv][nch][R]   base-2 domain: m2 + log2(l)
-  int H, Hkv, kq, R, G;
-  int max_seqlen, cache_stride, nch;
+  float* part_o;    // [B][Hkv][jmax][R][D]
+  float* part_lse;  // [B][Hkv][jmax][R]   base-2 domain: m2 + log2(l)
+  int32_t* seg_np;  // [B][Hkv]  pieces of each non-empty segment
+  int B, H, Hkv, kq, R, G;
+  int max_seqlen, cache_stride, jmax;
   float c2;  // scale * log2(e)
 };
 
 __device__ __forceinline__ int clamp_len(int s, int max_len) { return min(max(s, 0), max_len); }
 
+// Work is divided in "cost" units: a key costs 1, and starting a segment
+// piece costs kPieceCost more (the pipeline fill, the wave combine and the
+// partial write of a piece).  Segment s occupies cost [C_s, C_s + P + L_s):
+// its P start-up units, then its L_s keys.  A workgroup that takes the start
+// of a second segment thus gets that many fewer keys, and all workgroups
+// finish together.
+#ifndef ATTN_VERIFY_PIECE_COST
+#define ATTN_VERIFY_PIECE_COST 512
+#endif
+constexpr int kPieceCost = ATTN_VERIFY_PIECE_COST;
+
+// Maximum pieces of one segment: a segment of L keys meets at most
+// L / T + 2 slices of length T = ceil(total_cost / kSplitWgs), and
+// T >= Hkv * L / kSplitWgs.
+__host__ __device__ inline int max_pieces(int Hkv) { return (kSplitWgs + Hkv - 1) / Hkv + 2; }
+
+// Sequence lengths, wave-parallel: lane l holds the clamped length of
+// sequence base + l (0 past B).  One vector load instead of a chain of
+// dependent scalar loads.
+__device__ __forceinline__ int lane_length(const int32_t* seqlens, int B, int max_len, int base) {
+  const int b = base + (threadIdx.x & 63);
+  return b < B ? clamp_len(seqlens[b], max_len) : 0;
+}
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// Total cost over all segments (Hkv segments of length seqlens[b] per
+// non-empty sequence; the sum of the lengths is below 2^31, checked on the
+// host) and the slice length T = ceil(total_cost / kSplitWgs).
+__device__ __forceinline__ void slice_plan(const int32_t* seqlens, int B, int Hkv, int max_len,
+                                           long long& total, long long& T) {
+  int sum = 0, nonempty = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int x = lane_length(seqlens, B, max_len, b0);
+    sum += wave_sum(x);
+    nonempty += wave_sum(x > 0 ? 1 : 0);
+  }
+  total = ((long long)sum + (long long)nonempty * kPieceCost) * Hkv;
+  T = (total + kSplitWgs - 1) / kSplitWgs;
+}
+
 template <int D>
-__global__ void __launch_bounds__(kThreads, 2) verify_split_kernel(SplitArgs a) {
+__global__ void __launch_bounds__(kThreads, 1) verify_split_kernel(SplitArgs a) {
   constexpr int KS = D / 16;
   constexpr int NDB = D / 32;
-  __shared__ float red_o[kWaves][D][32];
+  constexpr int CPR = D / 8;
+  constexpr int STEP = kStep * D;              // elements per K (or V) stage
+  constexpr int INSN = STEP * 2 / 1024;        // 1 KB HBM->LDS loads per stage
+  constexpr int ROWS_PER_INSN = 1024 / (D * 2);
+  // Per wave: two stages of K and two of V, one LDS object per stage so the
+  // compiler can tell the next step's loads from this step's reads.
+  __shared__ __attribute__((aligned(1024))) uint16_t k_st0[kWaves][STEP];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_st1[kWaves][STEP];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_st0[kWaves][STEP];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_st1[kWaves][STEP];
   __shared__ float red_m[kWaves][32];
   __shared__ float red_l[kWaves][32];
+  __shared__ float red_lr[kWaves][32];
 
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int sk = clamp_len(a.seqlens[b], a.max_seqlen);
-  const int cstart = c * kChunk;
-  if (cstart >= sk) return;  // uniform over the workgroup
-  const int cend = min(sk, cstart + kChunk);
+  long long total, T;
+  slice_plan(a.seqlens, a.B, a.Hkv, a.max_seqlen, total, T);
+  if (blockIdx.x == 0 && threadIdx.x < 64) {
+    // empty segments have no piece: record 0 for the merge
+    for (int b0 = 0; b0 < a.B; b0 += 64) {
+      const int x = lane_length(a.seqlens, a.B, a.max_seqlen, b0);
+      if (b0 + (int)threadIdx.x < a.B && x == 0)
+        for (int g = 0; g < a.Hkv; ++g) a.seg_np[(b0 + threadIdx.x) * a.Hkv + g] = 0;
+    }
+  }
+  const long long lo = (long long)blockIdx.x * T;
+  const long long hi = min(lo + T, total);
+  if (lo >= hi) return;  // uniform over the workgroup
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
   // packed row n = (query head g*G + n / kq, new token n % kq)
   const bool row_ok = n < a.R;
   const int hh = n / a.kq, qi = n - hh * a.kq;
-  const int row_lim = sk - a.kq + qi;  // last visible key of this row
 
-  const uint16_t* Kb = a.k + (size_t)(b * a.Hkv + g) * a.cache_stride * D;
-  const uint16_t* Vb = a.v + (size_t)(b * a.Hkv + g) * a.cache_stride * D;
-
-  u32x4 qf[KS];
-  {
-    const uint16_t* qrow = a.q + ((size_t)(b * a.H + g * a.G + hh) * a.kq + qi) * D;
+  // HBM->LDS: instruction i of a stage covers stage rows
+  // [i*ROWS_PER_INSN, +ROWS_PER_INSN); lane l fills row i*ROWS_PER_INSN + l/CPR,
+  // chunk position l % CPR with global chunk (position ^ swizzle(row)).
+  uint32_t k_voff[INSN], v_voff[INSN];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = row_ok ? load16(qrow + ks * 16 + h * 8) : u32x4{0, 0, 0, 0};
+  for (int i = 0; i < INSN; ++i) {
+    const int row = i * ROWS_PER_INSN + lane / CPR;
+    const int pos = lane % CPR;
+    k_voff[i] = (row * D + ((pos ^ k_swz<D>(row)) * 8)) * 2;
+    v_voff[i] = (row * D + ((pos ^ v_swz<D>(row)) * 8)) * 2;
   }
+  // per-lane LDS byte offsets of the operand reads (see the prefill kernel)
+  const int gq = lane >> 4, r4 = (lane >> 2) & 3, c4 = lane & 3;
+  uint32_t k_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = (n * D + (((ks * 2 + h) ^ k_swz<D>(n)) * 8)) * 2;
+  uint32_t v_off[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int dcol = 32 * db + 16 * (gq & 1) + 4 * c4;
+    const int row = 4 * h + r4;
+    v_off[db] = (row * D + (((dcol >> 3) ^ v_swz<D>(row)) * 8) + (dcol & 7)) * 2;
+  }
+  typedef const __attribute__((address_space(3))) char lds_cchar;
 
-  f32x16 acc_o[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  // One piece: keys [k0, k1) of segment (b, g), whose length is sk; the
+  // partial goes to slot j of the segment.
+  auto piece = [&](int b, int g, int sk, int k0, int k1, int j) {
+    const int row_lim = sk - a.kq + qi;  // last visible key of this row
+    const uint16_t* Kb = a.k + (size_t)(b * a.Hkv + g) * a.cache_stride * D;
+    const uint16_t* Vb = a.v + (size_t)(b * a.Hkv + g) * a.cache_stride * D;
 
-  for (int j0 = cstart + wave * kStep; j0 < cend; j0 += kWaves * kStep) {
-    // ---- K operand: row j0 + n, eight head-dim values per step
-    u32x4 kf[KS];
-    const bool krow_ok = j0 + n < sk;
+    u32x4 qf[KS];
+    {
+      const uint16_t* qrow = a.q + ((size_t)(b * a.H + g * a.G + hh) * a.kq + qi) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      kf[ks] = krow_ok ? load16(Kb + (size_t)(j0 + n) * D + ks * 16 + h * 8) : u32x4{0, 0, 0, 0};
-    // ---- V segments: for each of the 16 keys this lane half needs, head
-    // dims [NDB*n, NDB*n + NDB)
-    uint32_t x[2][8][NDB / 2];
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = row_ok ? load16(qrow + ks * 16 + h * 8) : u32x4{0, 0, 0, 0};
+    }
+
+    // A step's buffer starts at its first key and ends at k1: rows past the
+    // piece read as zero, and a step past the end reads nothing.
+    auto issue = [&](int key0, const int ST) {
+      const int bytes = max(k1 - key0, 0) * D * 2;
+      const __amdgpu_buffer_rsrc_t kr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(Kb + (size_t)key0 * D), (short)0, bytes, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t vr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(Vb + (size_t)key0 * D), (short)0, bytes, kBufferWord3);
+      uint16_t* kd = ST ? k_st1[wave] : k_st0[wave];
+      uint16_t* vd = ST ? v_st1[wave] : v_st0[wave];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = j0 + 16 * t + 8 * (e / 4) + 4 * h + (e % 4);
-        const bool ok = key < sk;
-        const uint16_t* src = Vb + (size_t)key * D + NDB * n;
-        if constexpr (NDB == 4) {
-          const u32x2 w = ok ? *reinterpret_cast<const u32x2*>(src) : u32x2{0, 0};
-          x[t][e][0] = w[0];
-          x[t][e][1] = w[1];
-        } else {
-          x[t][e][0] = ok ? *reinterpret_cast<const uint32_t*>(src) : 0u;
-        }
+      for (int i = 0; i < INSN; ++i) {
+        buffer_load_lds16(kr, kd + i * 512, k_voff[i]);
+        buffer_load_lds16(vr, vd + i * 512, v_voff[i]);
       }
+    };
 
-    f32x16 s = f32x16{};
+    f32x16 acc_o[NDB];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) s = mfma_32x32x16_bf16(kf[ks], qf[ks], s);
+    for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
+    float m_ref = -INFINITY, l_run = 0.f, l_rnd = 0.f;
 
-    // mask keys past a row's limit (only the chunk's last steps need it)
-    if (j0 + kStep - 1 > sk - a.kq) {
+    auto compute = [&](int key0, const int ST) {
+      lds_cchar* kt = (lds_cchar*)(ST ? k_st1[wave] : k_st0[wave]);
+      lds_cchar* vt = (lds_cchar*)(ST ? v_st1[wave] : v_st0[wave]);
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 kf = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(kt + k_off[ks]);
+        s = mfma_32x32x16_bf16(kf, qf[ks], s);
+      }
+      // causal among the new tokens, end of the piece
+      if (key0 + kStep - 1 > sk - a.kq || key0 + kStep > k1) {
+        const int lim = min(row_lim, k1 - 1) - key0 - 4 * h;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r / 4) + (r % 4) > lim) s[r] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = max_halves(mx) * a.c2;
+      const bool raise = mx > m_ref + kRescaleSlack;
+      if (__builtin_expect(__any(raise), 0)) {
+        asm volatile("");
+        const float alpha = raise ? fast_exp2(m_ref - mx) : 1.f;  // 0 when m_ref = -inf
+        m_ref = raise ? mx : m_ref;
+        l_run *= alpha;
+        l_rnd *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+      }
+      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = j0 + 8 * (r / 4) + 4 * h + (r % 4);
-        if (key > row_lim || key >= sk) s[r] = -INFINITY;
+        s[r] = fast_exp2(fmaf(s[r], a.c2, -m_use));
+        l_run += s[r];
       }
-    }
-    float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    mx = fmaxf(mx, swap_halves(mx));
-    const float m_new = fmaxf(m_run, mx * a.c2);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float rs = 0.f;
+      for (int t = 0; t < 2; ++t) {
+        u32x4 pt;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = fast_exp2(fmaf(s[r], a.c2, -m_use));
-      s[r] = p;
-      rs += p;
+        for (int w = 0; w < 4; ++w) {
+          pt[w] = pack_bf16x2(s[8 * t + 2 * w], s[8 * t + 2 * w + 1]);
+          l_rnd = sum_bf16x2(pt[w], l_rnd);
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          lds_cchar* vb = vt + v_off[db] + 16 * t * D * 2;
+          const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)vb);
+          const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + 8 * D * 2));
+          u32x4 vf;
+          vf[0] = __builtin_bit_cast(u32x2, lo4)[0];
+          vf[1] = __builtin_bit_cast(u32x2, lo4)[1];
+          vf[2] = __builtin_bit_cast(u32x2, hi4)[0];
+          vf[3] = __builtin_bit_cast(u32x2, hi4)[1];
+          acc_o[db] = mfma_32x32x16_bf16(vf, pt, acc_o[db]);
+        }
+      }
+    };
+
+    // this wave's steps: key0 = k0 + kStep * (wave + kWaves * i).  Every step
+    // issues the next step's loads (past the end with an empty buffer: zeros
+    // land in the idle stage) so the loop has no branch and the counted wait
+    // is exact.
+    const int first = k0 + kStep * wave;
+    const int nsteps = first < k1 ? (k1 - first + kStep * kWaves - 1) / (kStep * kWaves) : 0;
+    auto step = [&](int i, const int ST) {
+      const int key0 = first + kStep * kWaves * i;
+      issue(key0 + kStep * kWaves, ST ^ 1);
+      wait_vmem_at_most<2 * INSN>();  // this step's loads landed, the next step's may fly
+      compute(key0, ST);
+    };
+    if (nsteps > 0) issue(first, 0);
+    for (int i = 0; i < nsteps; i += 2) {
+      step(i, 0);
+      if (i + 1 < nsteps) step(i + 1, 1);
     }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
+    wait_vmem_all();  // the last (empty) loads are done before the stages are reused
+
+    // ---- combine the waves through LDS.  Each wave parks its fp32
+    // accumulator [D][32] in its own two K stages (head dims < D/2 in stage 0,
+    // the rest in stage 1); no other wave touches them before the barrier.
+    auto red_at = [&](int w, int d) -> float* {
+      uint16_t* st = d < D / 2 ? k_st0[w] : k_st1[w];
+      return reinterpret_cast<float*>(st) + (d % (D / 2)) * 32;
+    };
+    static_assert(STEP * 2 >= (D / 2) * 32 * 4, "a K stage holds half of a wave's accumulator");
+    const float l_tot = sum_halves(l_run);
+    const float lr_tot = sum_halves(l_rnd);
+    if (h == 0) {
+      red_m[wave][n] = m_ref;
+      red_l[wave][n] = l_tot;
+      red_lr[wave][n] = lr_tot;
+    }
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
-
+      for (int r = 0; r < 16; ++r) {
+        const int d = 32 * db + 8 * (r / 4) + 4 * h + (r % 4);
+        red_at(wave, d)[n] = acc_o[db][r];
+      }
+    __syncthreads();
+    {
+      const int rn = tid & 31;  // packed row
+      const int dg = tid >> 5;  // group of DPT head dims
+      constexpr int DPT = D / (kThreads / 32);
+      float M = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      u32x4 pt;
-      pt[0] = pack_bf16x2(s[8 * t + 0], s[8 * t + 1]);
-      pt[1] = pack_bf16x2(s[8 * t + 2], s[8 * t + 3]);
-      pt[2] = pack_bf16x2(s[8 * t + 4], s[8 * t + 5]);
-      pt[3] = pack_bf16x2(s[8 * t + 6], s[8 * t + 7]);
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w][rn]);
+      const float M_use = (M == -INFINITY) ? 0.f : M;
+      float f[kWaves];
+      float L = 0.f, LR = 0.f;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        u32x4 vf;
+      for (int w = 0; w < kWaves; ++w) {
+        f[w] = fast_exp2(red_m[w][rn] - M_use);
+        L += f[w] * red_l[w][rn];
+        LR += f[w] * red_lr[w][rn];
+      }
+      if (rn < a.R) {
+        const size_t pidx = ((size_t)(b * a.Hkv + g) * a.jmax + j) * a.R + rn;
+        const float inv = LR > 0.f ? 1.f / LR : 0.f;
+        float* dst = a.part_o + pidx * D + dg * DPT;
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const uint32_t lo = x[t][2 * e2][db / 2], hi = x[t][2 * e2 + 1][db / 2];
-          vf[e2] = (db & 1) ? pack_hi16(lo, hi) : pack_lo16(lo, hi);
+        for (int d4 = 0; d4 < DPT; d4 += 4) {
+          f32x4 vv;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            float acc = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) acc = fmaf(f[w], red_at(w, dg * DPT + d4 + u)[rn], acc);
+            vv[u] = acc * inv;
+          }
+          *reinterpret_cast<f32x4*>(dst + d4) = vv;
         }
-        acc_o[db] = mfma_32x32x16_bf16(vf, pt, acc_o[db]);
+        if (dg == 0) a.part_lse[pidx] = L > 0.f ? M + fast_log2(L) : -INFINITY;
       }
     }
-  }
+    __syncthreads();  // the stages and red_* are free for the next piece
+  };
 
-  // ---- combine the four waves through LDS
-  const float l_tot = l_run + swap_halves(l_run);
-  if (h == 0) {
-    red_m[wave][n] = m_run;
-    red_l[wave][n] = l_tot;
-  }
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = 8 * (r / 4) + 4 * h + (r % 4);
-      red_o[wave][NDB * m + db][n] = acc_o[db][r];
-    }
-  __syncthreads();
-
-  {
-    const int rn = tid & 31;     // packed row
-    const int dg = tid >> 5;     // group of D/8 head dims
-    constexpr int DPT = D / 8;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w][rn]);
-    const float M_use = (M == -INFINITY) ? 0.f : M;
-    float f[kWaves];
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      f[w] = fast_exp2(red_m[w][rn] - M_use);
-      L += f[w] * red_l[w][rn];
-    }
-    if (rn < a.R) {
-      const size_t pidx = ((size_t)(b * a.Hkv + g) * a.nch + c) * a.R + rn;
-      const float inv = L > 0.f ? 1.f / L : 0.f;
-      float* dst = a.part_o + pidx * D + dg * DPT;
-#pragma unroll
-      for (int d4 = 0; d4 < DPT; d4 += 4) {
-        f32x4 vv;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          float acc = 0.f;
-#pragma unroll
-          for (int w = 0; w < kWaves; ++w) acc = fmaf(f[w], red_o[w][dg * DPT + d4 + u][rn], acc);
-          vv[u] = acc * inv;
+  // Walk the segments overlapping this workgroup's cost slice [lo, hi)
+  // (sequence-major, then KV head).
+  long long seq0 = 0;  // cost start of sequence b's Hkv segments
+  for (int b0 = 0; b0 < a.B && seq0 < hi; b0 += 64) {
+    const int len_l = lane_length(a.seqlens, a.B, a.max_seqlen, b0);
+    for (int bi = 0; bi < 64 && b0 + bi < a.B && seq0 < hi; ++bi) {
+      const int b = b0 + bi;
+      const int sk = __builtin_amdgcn_readlane(len_l, bi);
+      if (sk == 0) continue;
+      const long long seg = (long long)kPieceCost + sk;  // cost of one segment
+      if (seq0 + seg * a.Hkv > lo) {
+        for (int g = 0; g < a.Hkv; ++g) {
+          const long long c0 = seq0 + (long long)g * seg + kPieceCost;  // cost of key 0
+          const long long k0 = max(lo - c0, 0LL), k1 = min(hi - c0, (long long)sk);
+          if (k0 < k1) {
+            const int j = (int)((c0 + k0) / T - c0 / T);
+            if (j == 0 && tid == 0) a.seg_np[b * a.Hkv + g] = (int)(1 + (c0 + sk - 1) / T - c0 / T);
+            piece(b, g, sk, (int)k0, (int)k1, j);
+          }
         }
-        *reinterpret_cast<f32x4*>(dst + d4) = vv;
       }
-      if (dg == 0) a.part_lse[pidx] = L > 0.f ? M + fast_log2(L) : -INFINITY;
+      seq0 += seg * a.Hkv;
     }
   }
 }
@@ -216,14 +376,19 @@ __global__ void __launch_bounds__(kThreads, 2) verify_split_kernel(SplitArgs a) 
 struct MergeArgs {
   const float* part_o;
   const float* part_lse;
+  const int32_t* seg_np;
   const int32_t* seqlens;
   uint16_t* o;
   float* lse;
   int B, H, Hkv, kq, R, G;
-  int max_seqlen, nch;
+  int max_seqlen, jmax;
 };
 
-// One wave per (b, query head, new token): combine the chunk partials.
+// One wave per (b, query head, new token).  The split kernel recorded how
+// many pieces the row's segment has; the wave then issues every load it needs
+// at once (one piece LSE per lane, eight piece outputs per round), reduces
+// the LSEs and accumulates its head dims with the broadcast weights
+// exp2(LSE_p - LSE).
 template <int D>
 __global__ void __launch_bounds__(256) verify_merge_kernel(MergeArgs a) {
   constexpr int EPL = D / 64;  // head dims per lane
@@ -236,25 +401,70 @@ __global__ void __launch_bounds__(256) verify_merge_kernel(MergeArgs a) {
   const int b = row / (a.kq * a.H);
   const int g = hq / a.G, hh = hq - g * a.G;
   const int rn = hh * a.kq + qi;
-  const int sk = clamp_len(a.seqlens[b], a.max_seqlen);
-  const int nc = (sk + kChunk - 1) / kChunk;
-  const size_t base = (size_t)(b * a.Hkv + g) * a.nch;
-
-  float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, a.part_lse[(base + c) * a.R + rn]);
-  const float M_use = (M == -INFINITY) ? 0.f : M;
-  float L = 0.f;
+  // pieces of the row's segment (0 for an empty one; nothing was written
+  // when the split kernel did not run)
+  const int nc = a.max_seqlen > 0 ? min(a.seg_np[b * a.Hkv + g], a.jmax) : 0;
+  const size_t base = (size_t)(b * a.Hkv + g) * a.jmax;
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  for (int c = 0; c < nc; ++c) {
-    const size_t pidx = (base + c) * a.R + rn;
-    const float w = fast_exp2(a.part_lse[pidx] - M_use);
-    L += w;
-    const float* src = a.part_o + pidx * D + lane * EPL;
+  float M = -INFINITY, L = 0.f;
+  if (nc <= 8) {
+    // common case: the LSE (one per lane) and all eight outputs at once
+    const float lse_l = (lane < nc) ? a.part_lse[(base + lane) * a.R + rn] : -INFINITY;
+    float v[8][EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w, src[e], acc[e]);
+    for (int k = 0; k < 8; ++k) {
+      const float* src = a.part_o + ((base + min(k, max(nc - 1, 0))) * a.R + rn) * D + lane * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) v[k][e] = nc > 0 ? src[e] : 0.f;
+    }
+    M = lse_l;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    const float M_use = (M == -INFINITY) ? 0.f : M;
+    const float w = lane < nc ? fast_exp2(lse_l - M_use) : 0.f;
+    L = w;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float wk = __shfl(w, k, 64);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wk, v[k][e], acc[e]);
+    }
+  } else {
+    // pieces in rounds of 64 (one per lane)
+    const float lse_l = (lane < nc) ? a.part_lse[(base + lane) * a.R + rn] : -INFINITY;
+    M = lse_l;
+    for (int c0 = 64; c0 < nc; c0 += 64)
+      M = fmaxf(M, (c0 + lane < nc) ? a.part_lse[(base + c0 + lane) * a.R + rn] : -INFINITY);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    const float M_use = (M == -INFINITY) ? 0.f : M;
+    for (int c0 = 0; c0 < nc; c0 += 64) {
+      const float x = c0 == 0 ? lse_l : ((c0 + lane < nc) ? a.part_lse[(base + c0 + lane) * a.R + rn] : -INFINITY);
+      const float w = (c0 + lane < nc) ? fast_exp2(x - M_use) : 0.f;
+      L += w;
+      const int cn = min(64, nc - c0);
+      for (int k0 = 0; k0 < cn; k0 += 8) {
+        float v[8][EPL];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int kk = c0 + min(k0 + k, cn - 1);
+          const float* src = a.part_o + ((base + kk) * a.R + rn) * D + lane * EPL;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) v[k][e] = src[e];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float wk = __shfl(w, min(k0 + k, 63), 64) * (k0 + k < cn ? 1.f : 0.f);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wk, v[k][e], acc[e]);
+        }
+      }
+    }
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off, 64);
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint16_t* dst = a.o + ((size_t)(b * a.H + hq) * a.kq + qi) * D + lane * EPL;
   if constexpr (EPL == 2) {
@@ -274,10 +484,12 @@ template <int D>
 hipError_t launch(const VerifyArgs& p, hipStream_t s) {
   const int G = p.H / p.Hkv;
   const int R = G * p.kq;
-  const int nch = (p.max_seqlen_k + kChunk - 1) / kChunk;
-  const size_t n_parts = (size_t)p.B * p.Hkv * nch * R;
-  float* part_o = static_cast<float*>(p.workspace);
-  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(p.workspace) + align_up(n_parts * D * 4));
+  const int jmax = max_pieces(p.Hkv);
+  const size_t n_parts = (size_t)p.B * p.Hkv * jmax * R;
+  char* ws = static_cast<char*>(p.workspace);
+  float* part_o = reinterpret_cast<float*>(ws);
+  float* part_lse = reinterpret_cast<float*>(ws + align_up(n_parts * D * 4));
+  int32_t* seg_np = reinterpret_cast<int32_t*>(ws + align_up(n_parts * D * 4) + align_up(n_parts * 4));
 
   SplitArgs sa;
   sa.q = static_cast<const uint16_t*>(p.q);
@@ -286,6 +498,8 @@ hipError_t launch(const VerifyArgs& p, hipStream_t s) {
   sa.seqlens = p.seqlens;
   sa.part_o = part_o;
   sa.part_lse = part_lse;
+  sa.seg_np = seg_np;
+  sa.B = p.B;
   sa.H = p.H;
   sa.Hkv = p.Hkv;
   sa.kq = p.kq;
@@ -293,16 +507,17 @@ hipError_t launch(const VerifyArgs& p, hipStream_t s) {
   sa.G = G;
   sa.max_seqlen = p.max_seqlen_k;
   sa.cache_stride = p.cache_stride;
-  sa.nch = nch;
+  sa.jmax = jmax;
   sa.c2 = p.scale * kLog2e;
-  if (nch > 0) {
-    hipLaunchKernelGGL((verify_split_kernel<D>), dim3(nch, p.Hkv, p.B), dim3(kThreads), 0, s, sa);
+  if (p.max_seqlen_k > 0) {
+    hipLaunchKernelGGL((verify_split_kernel<D>), dim3(kSplitWgs), dim3(kThreads), 0, s, sa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   MergeArgs ma;
   ma.part_o = part_o;
   ma.part_lse = part_lse;
+  ma.seg_np = seg_np;
   ma.seqlens = p.seqlens;
   ma.o = static_cast<uint16_t*>(p.o);
   ma.lse = p.lse;
@@ -313,7 +528,7 @@ hipError_t launch(const VerifyArgs& p, hipStream_t s) {
   ma.R = R;
   ma.G = G;
   ma.max_seqlen = p.max_seqlen_k;
-  ma.nch = nch;
+  ma.jmax = jmax;
   const int rows = p.B * p.H * p.kq;
   hipLaunchKernelGGL((verify_merge_kernel<D>), dim3((rows + 3) / 4), dim3(256), 0, s, ma);
   return hipGetLastError();
@@ -321,12 +536,13 @@ hipError_t launch(const VerifyArgs& p, hipStream_t s) {
 
 }  // namespace
 
-int verify_chunk_keys() { return kChunk; }
+int verify_split_workgroups() { return kSplitWgs; }
 
-size_t verify_workspace_bytes(int B, int H, int kq, int d, int max_seqlen_k) {
-  const size_t nch = (size_t)((max_seqlen_k + kChunk - 1) / kChunk);
-  const size_t n_parts = (size_t)B * H * kq * nch;
-  return align_up(n_parts * d * 4) + align_up(n_parts * 4);
+size_t verify_workspace_bytes(int B, int H, int Hkv, int kq, int d) {
+  // fp32 O and LSE partials for every (sequence, query head, token, piece
+  // slot), and the piece count of every (sequence, KV head) segment
+  const size_t n_parts = (size_t)B * H * kq * max_pieces(Hkv);
+  return align_up(n_parts * d * 4) + align_up(n_parts * 4) + align_up((size_t)B * Hkv * 4);
 }
 
 hipError_t launch_verify_bf16(const VerifyArgs& p, hipStream_t s) {

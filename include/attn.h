@@ -59,8 +59,9 @@ extern "C" {
  * lse = ln(sum_j exp(scale * q_i.k_j)) over the visible keys, natural log of
  * the scaled logits.  A row with no visible key gets O = 0 and lse = -inf.
  * Rounding: O is rounded to nearest-even from fp32.  In the bf16 path the
- * probabilities are rounded to bf16 before the P.V product and the
- * denominator is summed from the unrounded fp32 values.
+ * probabilities are rounded to bf16 before the P.V product; O is divided by
+ * the sum of those rounded probabilities (its weights sum to one), and lse
+ * uses the sum of the unrounded fp32 probabilities.
  *
  * Sizes: B, Sq, Sk >= 0 (zero sizes are allowed; B*Sq == 0 is a no-op and a
  * pointer whose tensor is empty may be NULL); H, Hkv >= 1 with H % Hkv == 0;
@@ -72,10 +73,12 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * attn_verify_workspace_bytes -- bytes of device workspace attn_verify needs
- * for these sizes (fp32 partial outputs and LSEs of the key chunks plus
- * alignment).  Returns 0 for invalid sizes.
+ * for these sizes: fp32 partial outputs and LSEs for every (sequence, query
+ * head, new token, piece slot), where a segment (sequence, KV head) is cut
+ * into at most ceil(256 / Hkv) + 2 pieces, plus one int32 piece count per
+ * segment.  Independent of the cache lengths.  Returns 0 for invalid sizes.
  */
-size_t attn_verify_workspace_bytes(int B, int H, int kq, int d, int max_seqlen_k);
+size_t attn_verify_workspace_bytes(int B, int H, int Hkv, int kq, int d);
 
 /*
  * attn_verify -- attention of kq new query tokens per sequence against a
@@ -83,9 +86,11 @@ size_t attn_verify_workspace_bytes(int B, int H, int kq, int d, int max_seqlen_k
  * model scores all drafted positions in one pass ("FlashAttention,
  * speculative decoding, quantisation and parallelism", Mechanics /
  * Speculative decoding).  Computed as Flash-Decoding ("Making Decode Fast",
- * §5: split the keys across compute units, then a small final combine): a
- * split kernel writes a partial (O_c, LSE_c) per key chunk and a merge kernel
- * combines them with the two-block update of "Warmup Guide", Ch.3.
+ * §5: split the keys across compute units, then a small final combine): the
+ * keys of all (sequence, KV head) segments are cut into 256 equal slices, a
+ * split kernel writes a partial (O_p, LSE_p) per piece of segment in a slice,
+ * and a merge kernel combines the pieces with the two-block update of
+ * "Warmup Guide", Ch.3.
  *
  *   q                 [B, H, kq, d]                 bf16 (read)
  *   k_cache, v_cache  [B, Hkv, cache_stride, d]     bf16 (read; only the first

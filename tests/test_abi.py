@@ -88,7 +88,7 @@ def verify_args(**kw):
              kq=5, d=128, scale=0.088, dtype=bd.ATTN_BF16, ws=FAKE, wsb=None, stream=None)
     a.update(kw)
     if a["wsb"] is None:
-        a["wsb"] = bd.attn_verify_workspace_bytes(a["B"], a["H"], a["kq"], 128, a["maxs"])
+        a["wsb"] = bd.attn_verify_workspace_bytes(a["B"], a["H"], a["Hkv"], a["kq"], 128)
     return a
 
 
@@ -122,16 +122,16 @@ def test_verify_rejects(kw, code):
 
 
 def test_verify_workspace_formula():
-    # fp32 O and LSE partials for every (sequence, query head, token, chunk)
-    C = 1024
-    for B, H, kq, d, m in [(8, 32, 5, 128, 16025), (1, 8, 1, 64, 1), (2, 4, 3, 128, 1024), (2, 4, 3, 128, 1025)]:
-        nch = -(-m // C)
-        n = B * H * kq * nch
-        up = lambda x: -(-x // 256) * 256
-        assert bd.attn_verify_workspace_bytes(B, H, kq, d, m) == up(n * d * 4) + up(n * 4)
-    assert bd.attn_verify_workspace_bytes(1, 8, 5, 128, 0) == 0
-    assert bd.attn_verify_workspace_bytes(1, 8, 5, 96, 10) == 0
-    assert bd.attn_verify_workspace_bytes(-1, 8, 5, 128, 10) == 0
+    # fp32 O and LSE partials for every (sequence, query head, token, piece
+    # slot; a (sequence, KV head) segment has at most ceil(256/Hkv) + 2
+    # pieces) and one int32 piece count per segment
+    up = lambda x: -(-x // 256) * 256
+    for B, H, Hkv, kq, d in [(8, 32, 8, 5, 128), (1, 8, 1, 1, 64), (2, 4, 4, 3, 128), (3, 6, 3, 2, 64)]:
+        n = B * H * kq * (-(-256 // Hkv) + 2)
+        assert bd.attn_verify_workspace_bytes(B, H, Hkv, kq, d) == up(n * d * 4) + up(n * 4) + up(B * Hkv * 4)
+    assert bd.attn_verify_workspace_bytes(1, 8, 8, 5, 96) == 0
+    assert bd.attn_verify_workspace_bytes(-1, 8, 8, 5, 128) == 0
+    assert bd.attn_verify_workspace_bytes(1, 8, 3, 5, 128) == 0
 
 
 def test_verify_empty_batch_is_a_noop():

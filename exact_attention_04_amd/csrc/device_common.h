@@ -118,6 +118,17 @@ __device__ __forceinline__ void wait_vmem_at_most() {
 // Workgroup index remapped so that the workgroups the hardware sends to one
 // XCD (dispatch is round-robin over the 8 XCDs) get consecutive logical ids:
 // neighbouring tiles of one head then share that XCD's L2.
+// A wave-uniform value the compiler cannot prove uniform, moved to scalar
+// registers (buffer descriptors built from it then need no per-lane loop).
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ int xcd_grouped_block(int bid, int nblocks) {
   constexpr int kXcds = 8;
   if (nblocks % kXcds != 0) return bid;

@@ -9,25 +9,35 @@
 // parallelism", Mechanics / FlashAttention gives the same loop.
 //
 // Mapping onto CDNA4:
-//   * one workgroup = 4 waves = 128 query rows of one (batch, head); each wave
-//     owns 32 rows; K/V tiles of 64 keys are shared by the four waves through
-//     LDS, double-buffered and filled by direct HBM->LDS loads
-//     (global_load_lds_dwordx4), so the next tile streams in while the
-//     current one is consumed and no registers hold staged data;
-//   * scores are computed transposed, S^T = K Q^T, on the 32x32x16 bf16 MFMA,
-//     so each lane holds one query column and 32 of the tile's 64 keys: the
-//     row max is an in-lane reduction plus one exchange with the other wave
-//     half, and the row sum stays per lane until the end;
-//   * the output is accumulated transposed too, O^T += V^T P^T: P^T is the
-//     B operand straight from the score registers (rounded to bf16), the V^T
-//     A operand comes from row-major V with the LDS transpose read
-//     (ds_read_b64_tr_b16), and the rescale factor of a query is a per-lane
-//     scalar;
-//   * the softmax works in base 2 with scale*log2(e) folded into one FMA.
-//     The reference max of a row is only raised when the tile max exceeds it
-//     by more than 2^8 (the exponents then stay <= 8, far from overflow); the
-//     final O/l and LSE are unchanged by the choice of reference, as in Ch.3's
-//     rescaling identity, and most tiles skip the accumulator rescale;
+//   * one workgroup = 8 waves = 256 query rows of one (batch, head), 32 rows
+//     per wave; K/V tiles of 64 keys are shared by all eight waves through
+//     LDS, two (or three) buffers each, filled by direct HBM->LDS loads
+//     (buffer_load ... lds) issued one (or two) tiles ahead, so no registers
+//     hold staged data;
+//   * every tile is handled in two phases per wave: a matrix phase (scores of
+//     the next tile, S_{j+1}^T = K_{j+1} Q^T, and this tile's output update,
+//     O^T += V_j^T P_j^T, 32 MFMAs) and a vector phase (P_{j+1} from
+//     S_{j+1}: exponentials, sums, bf16 packing).  The waves form two groups
+//     of four, one wave of each group per SIMD, and the second group runs one
+//     phase behind the first: workgroup barriers separate the phases, so on
+//     every SIMD one wave keeps the matrix core busy while the other does its
+//     vector work, and the LDS reads of a tile come from one group at a time;
+//   * scores are computed transposed on the 32x32x16 bf16 MFMA, so each lane
+//     holds one query column and 32 of the tile's 64 keys; the output is
+//     accumulated transposed too: P^T is the B operand straight from the score
+//     registers (rounded to bf16), the V^T A operand comes from row-major V
+//     with the LDS transpose read (ds_read_b64_tr_b16), and the rescale
+//     factor of a query is a per-lane scalar;
+//   * the softmax works in base 2 with scale*log2(e) folded into one FMA,
+//     against a per-row reference value m_ref instead of the exact running
+//     max: the final O/l and LSE do not depend on the reference (Ch.3's
+//     rescaling identity), only overflow does.  A tile is exponentiated
+//     against the current m_ref without computing its max; only when a
+//     lane's tile sum exceeds 2^32 (some score is > m_ref + 27 in log2
+//     units) or a row has no reference yet does the wave take a slow path
+//     that computes the tile max, raises m_ref, rescales the accumulator and
+//     exponentiates again.  Probabilities stay below 2^32, far from fp32 and
+//     bf16 overflow, and most tiles need neither a max nor a rescale;
 //   * two denominators are kept: the fp32 sum of the probabilities (for LSE)
 //     and the sum of the same probabilities rounded to bf16, i.e. of exactly
 //     the weights the P.V product used (one v_dot2 per pair).  O is divided by
@@ -40,32 +50,38 @@
 namespace attn {
 namespace {
 
-// Tile shape (build-time constants): waves per workgroup (32 query rows
-// each), keys per K/V tile, and whether matrix-core clusters raise the wave's
-// issue priority so they are not starved by the other wave's softmax.
-#ifndef ATTN_FWD_WAVES
-#define ATTN_FWD_WAVES 4
-#endif
-#ifndef ATTN_FWD_BC
-#define ATTN_FWD_BC 64
-#endif
+// Whether a wave raises its issue priority during its matrix phase, and
+// the number of LDS buffers per K/V tile stream (2 or 3).
 #ifndef ATTN_FWD_PRIO
-#define ATTN_FWD_PRIO 1
+#define ATTN_FWD_PRIO 0
 #endif
-#ifndef ATTN_FWD_SCHED
-#define ATTN_FWD_SCHED 0
+#ifndef ATTN_FWD_STAGES
+#define ATTN_FWD_STAGES 2
 #endif
-#ifndef ATTN_FWD_QB
-#define ATTN_FWD_QB 1
+// Whether the sum of the bf16-rounded probabilities comes from the matrix
+// cores (an all-ones block appended to V^T) instead of v_dot2 on the VALU.
+#ifndef ATTN_FWD_MFMA_LSUM
+#define ATTN_FWD_MFMA_LSUM 0
 #endif
-constexpr int kWaves = ATTN_FWD_WAVES;
-constexpr int kQb = ATTN_FWD_QB;  // 32-query blocks per wave
+// Matrix phase schedule: how many MFMAs ahead the LDS operand reads are
+// issued (0: leave it to the compiler), and whether the phase boundaries are
+// scheduling fences (PIN).
+#ifndef ATTN_FWD_KPRE
+#define ATTN_FWD_KPRE 4
+#endif
+#ifndef ATTN_FWD_PIN
+#define ATTN_FWD_PIN 1
+#endif
+constexpr int kStages = ATTN_FWD_STAGES;
+static_assert(kStages == 2 || kStages == 3, "two or three tile buffers");
+constexpr int kWaves = 8;               // two groups of four, one wave of each per SIMD
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBr = 32 * kQb * kWaves;  // query rows per workgroup
-constexpr int kBc = ATTN_FWD_BC;  // keys per K/V tile
-constexpr int kNkb = kBc / 32;    // 32-key blocks per tile
-constexpr int kMinBlocks = (kQb == 1 ? 8 : 4) / kWaves;  // waves per SIMD: 2 (one query block) or 1
-constexpr float kRescaleSlack = 8.0f;  // log2 units
+constexpr int kBr = 32 * kWaves;        // query rows per workgroup
+constexpr int kBc = 64;                 // keys per K/V tile
+constexpr int kNkb = kBc / 32;          // 32-key blocks per tile
+constexpr int kNt = kBc / 16;           // 16-key MFMA steps per tile
+constexpr float kRescaleSlack = 8.0f;   // log2 units
+constexpr float kTileSumLimit = 0x1p32f;  // fast-path bound on a lane's tile sum
 
 struct FwdKernelArgs {
   const uint16_t* q;
@@ -78,35 +94,76 @@ struct FwdKernelArgs {
   float c2;  // scale * log2(e)
 };
 
-__device__ __forceinline__ void prio_high() {
+// Workgroup barrier for the phase hand-over: this wave's LDS reads have
+// completed and no instruction is scheduled across it (a matrix
+// instruction that slipped into the vector phase would compete with the
+// other wave's), but HBM->LDS loads still in flight are not waited for (a
+// fence would wait for them too: they write LDS); where a tile must have
+// landed, vmcnt is waited for explicitly first.
+__device__ __forceinline__ void lds_barrier() {
+  if (ATTN_FWD_PIN) __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (ATTN_FWD_PIN) __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void prio_matrix() {
   if (ATTN_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
 }
-__device__ __forceinline__ void prio_low() {
+__device__ __forceinline__ void prio_vector() {
   if (ATTN_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
 }
 
+// Scheduling pipeline of a matrix phase: KM score MFMAs (one K read each)
+// then VM output MFMAs (two V transpose reads each), with the LDS reads
+// issued L MFMAs ahead of the MFMA that consumes them.
+template <int KM, int VM>
+__device__ constexpr int reads_needed(int i) {  // reads consumed by MFMAs 0..i
+  return i < KM ? i + 1 : KM + 2 * (i - KM + 1);
+}
+template <int I, int KM, int VM, int L>
+__device__ __forceinline__ void matrix_pipeline() {
+  if constexpr (I < KM + VM) {
+    constexpr int last = KM + VM - 1;
+    constexpr int hi = I + L < last ? I + L : last;
+    constexpr int lo = I == 0 ? 0 : (I - 1 + L < last ? reads_needed<KM, VM>(I - 1 + L) : reads_needed<KM, VM>(last));
+    constexpr int n = reads_needed<KM, VM>(hi) - lo;
+    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, 0);  // LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                        // one MFMA
+    matrix_pipeline<I + 1, KM, VM, L>();
+  }
+}
+
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kThreads, kMinBlocks) fwd_bf16_kernel(FwdKernelArgs a) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fwd_bf16_kernel(FwdKernelArgs a) {
   constexpr int CPR = D / 8;   // 16-byte chunks per K/V row
   constexpr int KS = D / 16;   // MFMA steps over the head dim for S^T
   constexpr int NDB = D / 32;  // 32-row blocks of O^T (head dim)
-  constexpr int QB = kQb;      // 32-query column blocks per wave
   constexpr int TILE = kBc * D;  // elements per K or V tile
   constexpr int ROWS_PER_INSN = 1024 / (D * 2);  // rows one wave-wide 1 KB load covers
   constexpr int INSN_PER_WAVE = TILE * 2 / 1024 / kWaves;
+  static_assert(INSN_PER_WAVE >= 1, "every wave loads part of each tile");
 
-  // one LDS object per buffer, so the compiler can prove that loads into one
-  // buffer never alias reads of the other
+  // kStages buffers each for K and V tiles, one LDS object per buffer, so
+  // the compiler can prove that loads into one buffer never alias reads of
+  // another
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds2[kStages > 2 ? TILE : 1];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds2[kStages > 2 ? TILE : 1];
+  auto kbuf = [&](const int I) __attribute__((always_inline)) { return I == 0 ? k_lds0 : I == 1 ? k_lds1 : k_lds2; };
+  auto vbuf = [&](const int I) __attribute__((always_inline)) { return I == 0 ? v_lds0 : I == 1 ? v_lds1 : v_lds2; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
-  const int n = lane & 31;  // query column within a 32-row block
+  const int n = lane & 31;  // query column within the wave's 32 rows
   const int h = lane >> 5;  // wave half
+  // Waves w and w + 4 share a SIMD; w < 4 leads, w >= 4 trails by one phase.
+  // Their row blocks interleave so both groups reach the same last key.
+  const bool lead = wave < 4;
+  const int rb = 2 * (wave & 3) + (lead ? 0 : 1);
 
   const int blk = xcd_grouped_block(blockIdx.x, gridDim.x);
   const int bh = blk / a.nqb;
@@ -117,24 +174,28 @@ __global__ void __launch_bounds__(kThreads, kMinBlocks) fwd_bf16_kernel(FwdKerne
   const int g = hq / (a.H / a.Hkv);
 
   const int q0 = qblk * kBr;
-  const int wq0 = q0 + wave * 32 * QB;  // first query row of this wave
-  const int shift = a.Sk - a.Sq;        // bottom-right causal alignment
+  const int wq0 = q0 + 32 * rb;   // first query row of this wave
+  const int shift = a.Sk - a.Sq;  // bottom-right causal alignment
 
   const uint16_t* Q = a.q + (size_t)(b * a.H + hq) * a.Sq * D;
-  const uint16_t* K = a.k + (size_t)(b * a.Hkv + g) * a.Sk * D;
-  const uint16_t* V = a.v + (size_t)(b * a.Hkv + g) * a.Sk * D;
+  const uint16_t* K = uniform_ptr(a.k + (size_t)(b * a.Hkv + g) * a.Sk * D);
+  const uint16_t* V = uniform_ptr(a.v + (size_t)(b * a.Hkv + g) * a.Sk * D);
 
+  // tiles the workgroup visits (every wave runs all of them: the phases are
+  // workgroup-wide); tiles [0, nfull) need no mask for this wave's rows
   int kend = a.Sk;
   if (CAUSAL) kend = min(a.Sk, min(q0 + kBr, a.Sq) + shift);
   kend = max(kend, 0);
   const int nkt = (kend + kBc - 1) / kBc;
+  int nfull = a.Sk / kBc;
+  if (CAUSAL) nfull = min(nfull, max(wq0 + shift + 1, 0) / kBc);
 
-  // ---- direct HBM -> LDS tile loads (buffer_load ... lds).  Wave-wide
-  // instruction i of this wave fills LDS bytes [1024*(wave*INSN_PER_WAVE+i),
-  // +1024); lane l's 16 bytes land at offset 16*l, i.e. tile row
-  // r = first row + l / CPR, chunk position l % CPR, which holds global chunk
-  // (position ^ swizzle(r)).  The buffer descriptor of a tile starts at its
-  // first key and ends at key Sk, so rows past Sk read as zeros.
+  // ---- direct HBM -> LDS tile loads.  Wave-wide instruction i of this wave
+  // fills LDS bytes [1024*(wave*INSN_PER_WAVE+i), +1024); lane l's 16 bytes
+  // land at offset 16*l, i.e. tile row r = first row + l / CPR, chunk position
+  // l % CPR, which holds global chunk (position ^ swizzle(r)).  The buffer
+  // descriptor of a tile starts at its first key and ends at key Sk, so rows
+  // past Sk read as zeros.
   uint32_t k_voff[INSN_PER_WAVE], v_voff[INSN_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < INSN_PER_WAVE; ++i) {
@@ -143,30 +204,23 @@ __global__ void __launch_bounds__(kThreads, kMinBlocks) fwd_bf16_kernel(FwdKerne
     k_voff[i] = (row * D + ((pos ^ k_swz<D>(row)) * 8)) * 2;
     v_voff[i] = (row * D + ((pos ^ v_swz<D>(row)) * 8)) * 2;
   }
-  // Q^T as the B operand: column n of block qb = query wq0 + 32qb + n, eight
-  // head-dim values per step.
-  u32x4 qf[QB][KS];
+  // Q^T as the B operand: column n = query wq0 + n, eight head-dim values per
+  // step.
+  u32x4 qf[KS];
+  {
+    const int qrow = wq0 + n;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = wq0 + 32 * qb + n;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      qf[qb][ks] = (qrow < a.Sq) ? load16(Q + (size_t)qrow * D + ks * 16 + h * 8) : u32x4{0, 0, 0, 0};
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = (qrow < a.Sq) ? load16(Q + (size_t)qrow * D + ks * 16 + h * 8) : u32x4{0, 0, 0, 0};
   }
 
-  f32x16 acc_o[QB][NDB];
+  f32x16 acc_o[NDB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) acc_o[qb][db] = f32x16{};
-  float m_ref[QB], l_run[QB], l_rnd[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_ref[qb] = -INFINITY;  // reference max, base-2 domain (scaled logits * log2 e)
-    l_run[qb] = 0.f;        // running denominator, this lane's keys only
-    l_rnd[qb] = 0.f;        // same, of the bf16-rounded probabilities
-  }
+  for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
+  float m_ref = -INFINITY;  // reference max, base-2 domain (scaled logits * log2 e)
+  float l_run = 0.f;        // running denominator, this lane's keys only
+  float l_rnd = 0.f;        // same, of the bf16-rounded probabilities
+  f32x16 acc_l = f32x16{};  // with the MFMA sum: every register holds l_rnd of the lane's query
 
   // Per-lane LDS byte offsets, fixed for the whole kernel (buffer and tile
   // offsets are immediates).  K A-operand of block kb, step ks: row
@@ -187,123 +241,107 @@ __global__ void __launch_bounds__(kThreads, kMinBlocks) fwd_bf16_kernel(FwdKerne
   }
   typedef const __attribute__((address_space(3))) char lds_cchar;
 
-  // Tiles [0, nfull) need no mask for any row of this workgroup; the rest
-  // (causal diagonal, ragged tail) are masked.
-  int nfull = a.Sk / kBc;
-  if (CAUSAL) nfull = min(nfull, max(q0 + shift + 1, 0) / kBc);
+  f32x16 s[kNkb];  // scores of the next tile (fp32)
+  u32x4 pt[kNt];   // probabilities of the current tile, bf16, as MFMA B operands
 
-  // Software pipeline.  Iteration j consumes K_{j+1} (scores of the next
-  // tile) and V_j (output of this tile), so the matrix cores compute
-  // S_{j+1} = K_{j+1} Q^T while the vector ALUs turn S_j into P_j, then
-  // O += V_j^T P_j.  Score registers and LDS buffers alternate with the tile
-  // parity: tile t's scores live in sreg[t & 1], its K in kbuf[t & 1], its V
-  // in vbuf[t & 1].
-  f32x16 sreg[2][QB][kNkb];
-
-  auto scores = [&](f32x16 (&s)[QB][kNkb], const int KBUF) {
-    lds_cchar* k_base = (lds_cchar*)(KBUF ? k_lds1 : k_lds0);
+  // S^T of a tile from kbuf[KBUF]; the two 32-key blocks alternate so that
+  // consecutive MFMAs never depend on each other
+  auto scores = [&](const int KBUF) __attribute__((always_inline)) {
+    lds_cchar* k_base = (lds_cchar*)kbuf(KBUF);
 #pragma unroll
-    for (int kb = 0; kb < kNkb; ++kb) {
+    for (int kb = 0; kb < kNkb; ++kb) s[kb] = f32x16{};
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[qb][kb] = f32x16{};
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+      for (int kb = 0; kb < kNkb; ++kb) {
         const u32x4 kf = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
             k_base + k_off[ks] + kb * 32 * D * 2);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma_32x32x16_bf16(kf, qf[qb][ks], s[qb][kb]);
+        s[kb] = mfma_32x32x16_bf16(kf, qf[ks], s[kb]);
       }
     }
   };
 
   // hide keys past a row's last visible key (causal diagonal, ragged tail)
-  auto mask = [&](f32x16 (&s)[QB][kNkb], int j0) {
+  auto mask = [&](int j0) __attribute__((always_inline)) {
+    const int qrow = wq0 + n;
+    const int lim = (CAUSAL ? min(a.Sk - 1, qrow + shift) : a.Sk - 1) - j0 - 4 * h;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int qrow = wq0 + 32 * qb + n;
-      const int lim = (CAUSAL ? min(a.Sk - 1, qrow + shift) : a.Sk - 1) - j0 - 4 * h;
+    for (int kb = 0; kb < kNkb; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < kNkb; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (kb * 32 + 8 * (r / 4) + (r % 4) > lim) s[qb][kb][r] = -INFINITY;
-        }
-    }
+      for (int r = 0; r < 16; ++r) {
+        if (kb * 32 + 8 * (r / 4) + (r % 4) > lim) s[kb][r] = -INFINITY;
+      }
   };
 
-  // row max of a score tile (base-2 domain)
-  auto rowmax = [&](f32x16 (&s)[QB][kNkb], float (&mx)[QB]) {
+  // slow path: raise the reference to the tile max where it exceeds it by
+  // more than the slack (or where there was none), rescaling what was
+  // accumulated
+  auto raise_ref = [&]() __attribute__((always_inline)) {
+    float mx = -INFINITY;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      mx[qb] = -INFINITY;
+    for (int kb = 0; kb < kNkb; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < kNkb; ++kb)
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = max_halves(mx) * a.c2;
+    const bool raise = mx > m_ref + kRescaleSlack || (m_ref == -INFINITY && mx > -INFINITY);
+    const float alpha = raise ? fast_exp2(m_ref - mx) : 1.f;  // 0 when m_ref = -inf
+    m_ref = raise ? mx : m_ref;
+    l_run *= alpha;
+    l_rnd *= alpha;
+    if (ATTN_FWD_MFMA_LSUM) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx[qb] = fmaxf(mx[qb], s[qb][kb][r]);
-      mx[qb] = max_halves(mx[qb]) * a.c2;
+      for (int r = 0; r < 16; ++r) acc_l[r] *= alpha;
     }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
   };
 
-  // raise the reference max where the tile max exceeds it by more than the
-  // slack (rare: a real branch around the accumulator rescale)
-  auto raise_ref = [&](const float (&mx)[QB]) {
-    bool raise_any = false;
+  // One pass over the score tile (left intact): probabilities against the
+  // reference, their fp32 sum ts, the bf16-rounded values packed as the B
+  // operands of the P.V product, and the sum tr of the rounded values.
+  // Partial sums run in several chains so the adds do not serialise.
+  auto softmax = [&](float& ts, float& tr) __attribute__((always_inline)) {
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;  // nothing visible yet
+    float a4[4] = {0.f, 0.f, 0.f, 0.f};
+    float r2[2] = {0.f, 0.f};
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) raise_any |= mx[qb] > m_ref[qb] + kRescaleSlack;
-    if (__builtin_expect(__any(raise_any), 0)) {
+    for (int t = 0; t < kNt; ++t) {
+      const int kb = t >> 1, base = (t & 1) * 8;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float p0 = fast_exp2(fmaf(s[kb][base + 2 * w], a.c2, -m_use));
+        const float p1 = fast_exp2(fmaf(s[kb][base + 2 * w + 1], a.c2, -m_use));
+        a4[(2 * w) & 3] += p0;
+        a4[(2 * w + 1) & 3] += p1;
+        pt[t][w] = pack_bf16x2(p0, p1);
+        if (!ATTN_FWD_MFMA_LSUM) r2[w & 1] = sum_bf16x2(pt[t][w], r2[w & 1]);
+      }
+    }
+    ts = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+    tr = r2[0] + r2[1];
+  };
+  // P of the score tile, with the slow path when the fast one may overflow
+  // or a row has no reference yet; then the tile's sums join the running ones
+  auto probabilities = [&]() __attribute__((always_inline)) {
+    float ts, tr;
+    softmax(ts, tr);
+    const bool bad = !(ts <= kTileSumLimit) || m_ref == -INFINITY;
+    if (__builtin_expect(__any(bad), 0)) {
       asm volatile("");
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const bool raise = mx[qb] > m_ref[qb] + kRescaleSlack;
-        const float alpha = raise ? fast_exp2(m_ref[qb] - mx[qb]) : 1.f;  // 0 when m_ref = -inf
-        m_ref[qb] = raise ? mx[qb] : m_ref[qb];
-        l_run[qb] *= alpha;
-        l_rnd[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc_o[qb][db][r] *= alpha;
-      }
+      raise_ref();
+      softmax(ts, tr);
     }
+    l_run += ts;
+    l_rnd += tr;
   };
 
-  constexpr int NT = kBc / 16;  // 16-key MFMA steps per tile
-  // probabilities in place (fp32), rounded to bf16 and packed as the B
-  // operands of the P.V product; the sum of the rounded values
-  auto exponentiate = [&](f32x16 (&s)[QB][kNkb], u32x4 (&pt)[QB][NT]) {
+  // O^T += V^T P^T over the tile's 16-key steps
+  auto accumulate = [&](const int VBUF) __attribute__((always_inline)) {
+    lds_cchar* v_base = (lds_cchar*)vbuf(VBUF);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float m_use = (m_ref[qb] == -INFINITY) ? 0.f : m_ref[qb];  // nothing visible yet
-#pragma unroll
-      for (int kb = 0; kb < kNkb; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[qb][kb][r] = fast_exp2(fmaf(s[qb][kb][r], a.c2, -m_use));
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int kb = t >> 1, base = (t & 1) * 8;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          pt[qb][t][w] = pack_bf16x2(s[qb][kb][base + 2 * w], s[qb][kb][base + 2 * w + 1]);
-          l_rnd[qb] = sum_bf16x2(pt[qb][t][w], l_rnd[qb]);
-        }
-      }
-    }
-  };
-  // fp32 sum of the (unrounded) probabilities
-  auto sum_p = [&](f32x16 (&s)[QB][kNkb]) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < kNkb; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) l_run[qb] += s[qb][kb][r];
-  };
-
-  // O^T += V^T P^T over the tile's 16-key steps; each V read feeds all QB blocks
-  auto accumulate = [&](const u32x4 (&pt)[QB][NT], const int VBUF) {
-    lds_cchar* v_base = (lds_cchar*)(VBUF ? v_lds1 : v_lds0);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
+    for (int t = 0; t < kNt; ++t) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         // items 0..3: keys 16t + 4h + r4; items 4..7: keys 16t + 8 + 4h + r4
@@ -315,122 +353,134 @@ __global__ void __launch_bounds__(kThreads, kMinBlocks) fwd_bf16_kernel(FwdKerne
         vf[1] = __builtin_bit_cast(u32x2, lo)[1];
         vf[2] = __builtin_bit_cast(u32x2, hi)[0];
         vf[3] = __builtin_bit_cast(u32x2, hi)[1];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) acc_o[qb][db] = mfma_32x32x16_bf16(vf, pt[qb][t], acc_o[qb][db]);
+        acc_o[db] = mfma_32x32x16_bf16(vf, pt[t], acc_o[db]);
+      }
+      if (ATTN_FWD_MFMA_LSUM) {
+        const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0 pairs
+        acc_l = mfma_32x32x16_bf16(ones, pt[t], acc_l);
       }
     }
   };
 
-  // DMA of K tile t into kbuf[t & 1] / V tile t into vbuf[t & 1]
-  auto issue_k = [&](int t, const int BUF) {
+  // this wave's share of K tile t into kbuf[BUF] / V tile t into vbuf[BUF];
+  // a tile at or past Sk has an empty descriptor (every lane reads zeros),
+  // so a round always issues the same number of loads
+  auto issue_k = [&](int t, const int BUF) __attribute__((always_inline)) {
     const int j0 = t * kBc;
     const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(K + (size_t)j0 * D), (short)0, (a.Sk - j0) * D * 2, kBufferWord3);
-    uint16_t* kd = BUF ? k_lds1 : k_lds0;
+        (void*)(K + (size_t)j0 * D), (short)0, max(a.Sk - j0, 0) * D * 2, kBufferWord3);
+    uint16_t* kd = kbuf(BUF);
 #pragma unroll
     for (int i = 0; i < INSN_PER_WAVE; ++i) buffer_load_lds16(kr, kd + (wave * INSN_PER_WAVE + i) * 512, k_voff[i]);
   };
-  auto issue_v = [&](int t, const int BUF) {
+  auto issue_v = [&](int t, const int BUF) __attribute__((always_inline)) {
     const int j0 = t * kBc;
     const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(V + (size_t)j0 * D), (short)0, (a.Sk - j0) * D * 2, kBufferWord3);
-    uint16_t* vd = BUF ? v_lds1 : v_lds0;
+        (void*)(V + (size_t)j0 * D), (short)0, max(a.Sk - j0, 0) * D * 2, kBufferWord3);
+    uint16_t* vd = vbuf(BUF);
 #pragma unroll
     for (int i = 0; i < INSN_PER_WAVE; ++i) buffer_load_lds16(vr, vd + (wave * INSN_PER_WAVE + i) * 512, v_voff[i]);
   };
-
-  // Scheduling hints: interleave each region's matrix instructions with its
-  // vector/LDS work so the MFMA pipe stays fed from a single wave.
-  constexpr int MF1 = kNkb * KS * QB;   // S MFMAs per tile
-  constexpr int MF2 = NT * NDB * QB;    // P.V MFMAs per tile
-  constexpr int V1 = (kNkb * 16 * 2 + NT * 8) * QB;  // fma+exp, pack+sum per tile
-  constexpr int V2 = kNkb * 16 * QB + kNkb * 8 * QB; // fp32 sums + max3
-  auto interleave1 = [&]() {
-    if (!ATTN_FWD_SCHED) return;
-#pragma unroll
-    for (int i = 0; i < MF1 / QB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);             // MFMA (one K operand)
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);              // K operand read
-      __builtin_amdgcn_sched_group_barrier(0x002, V1 * QB / MF1, 0);  // VALU
-    }
-  };
-  auto interleave2 = [&]() {
-    if (!ATTN_FWD_SCHED) return;
-#pragma unroll
-    for (int i = 0; i < MF2 / QB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);                       // MFMA (one V operand)
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                        // V^T transpose reads
-      __builtin_amdgcn_sched_group_barrier(0x002, (V2 * QB + MF2 - 1) / MF2, 0);  // VALU
-    }
+  // Loads of round j (S = kStages): K_{j+S} into kbuf[j % S] (K_j's, read
+  // for the last time in round j-1) and V_{j+S-1} into vbuf[(j-1) % S]
+  // (V_{j-1}'s, likewise); issued once both groups have finished round
+  // j-1's matrix phase, needed by round j+S-1's.  Each round issues kLoads
+  // instructions per wave; the waits leave the latest (S-2) rounds' loads in
+  // flight, so each load has 2(S-1) phases to land.
+  constexpr int kLoads = 2 * INSN_PER_WAVE;
+  constexpr int kInFlight = (kStages - 2) * kLoads;
+  auto issue = [&](int j, const int P) __attribute__((always_inline)) {
+    issue_k(j + kStages, P);
+    issue_v(j + kStages - 1, (P + kStages - 1) % kStages);
   };
 
-  // Iteration j (P = j & 1, a literal at every call): scores of tile j are in
-  // sreg[P] with the reference max already raised; K_{j+1} is in kbuf[P^1],
-  // V_j in vbuf[P].
-  auto step = [&](int j, const int P) {
-    if (j + 2 < nkt) issue_k(j + 2, P);      // K_j's buffer was last read in iteration j-1
-    if (j + 1 < nkt) issue_v(j + 1, P ^ 1);  // V_{j-1}'s buffer likewise
-    u32x4 pt[QB][NT];
-    // region 1: S_{j+1} on the matrix cores, P_j on the vector ALUs
-    scores(sreg[P ^ 1], P ^ 1);
-    exponentiate(sreg[P], pt);
-    interleave1();
-    // region 2: O += V_j^T P_j, the fp32 sums of P_j and the max of S_{j+1}
-    accumulate(pt, P);
-    sum_p(sreg[P]);
-    float mx[QB];
-    rowmax(sreg[P ^ 1], mx);
-    interleave2();
-    if (j + 1 >= nfull) {  // rare: the next tile is on the diagonal or the tail
-      mask(sreg[P ^ 1], (j + 1) * kBc);
-      rowmax(sreg[P ^ 1], mx);
+  // Round j (P = j % S, a literal at every call).  Matrix phase: S_{j+1}
+  // from kbuf[(P+1) % S] (unless j is the last tile) and O += V_j^T P_j
+  // from vbuf[P].  Vector phase: P_{j+1} from S_{j+1}, masked first if
+  // MASKED (a literal) and the tile needs it.  The leading group (LEAD) runs
+  //   issue(j) | matrix | barrier | vector | wait | barrier
+  // and the trailing group, whose phases sit one barrier later,
+  //   matrix | wait | barrier | issue(j+1) | vector | barrier,
+  // where each wait leaves only the loads of the round's own issue in
+  // flight, so every load has landed, in every wave, by the barrier that
+  // precedes the first matrix phase reading it.
+  // Order of the matrix phase: each LDS operand read is issued KPRE MFMAs
+  // before the MFMA that consumes it, so LDS latency hides behind matrix
+  // work (0 leaves the order to the compiler).
+  auto matrix_schedule = [&]() __attribute__((always_inline)) {
+    if constexpr (ATTN_FWD_KPRE > 0) matrix_pipeline<0, kNkb * KS, kNt * NDB, ATTN_FWD_KPRE>();
+  };
+
+  auto round = [&](int j, const int P, const bool MASKED, const bool LEAD) __attribute__((always_inline)) {
+    const bool more = !MASKED || j + 1 < nkt;  // rounds of the plain loop always have a next tile
+    if (LEAD) issue(j, P);
+    prio_matrix();
+    if (more) scores((P + 1) % kStages);
+    accumulate(P);
+    if (!MASKED) matrix_schedule();
+    prio_vector();
+    if (!LEAD) wait_vmem_at_most<kInFlight>();
+    lds_barrier();
+    if (!LEAD) issue(j + 1, (P + 1) % kStages);
+    if (more) {
+      if (MASKED && j + 1 >= nfull) mask((j + 1) * kBc);
+      probabilities();
     }
-    raise_ref(mx);
+    if (LEAD) wait_vmem_at_most<kInFlight>();
+    lds_barrier();
+  };
+
+  // The whole tile loop of one group (LEAD a literal: each group gets its
+  // own straight-line code, so the compiler can see which LDS buffer every
+  // read and every HBM->LDS load touches).
+  auto run = [&](const bool LEAD) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < kStages; ++t) issue_k(t, t);
+#pragma unroll
+    for (int t = 0; t + 1 < kStages; ++t) issue_v(t, t);
     wait_vmem_all();
-    __syncthreads();
-  };
-  // last tile: no next scores
-  auto last = [&](const int P) {
-    u32x4 pt[QB][NT];
-    exponentiate(sreg[P], pt);
-    accumulate(pt, P);
-    sum_p(sreg[P]);
+    lds_barrier();
+    scores(0);
+    if (0 >= nfull) mask(0);
+    if (LEAD) probabilities();
+    lds_barrier();
+    if (!LEAD) {
+      issue(0, 0);
+      probabilities();
+      lds_barrier();
+    }
+    // Rounds j < nplain produce an S_{j+1} that needs no mask for this
+    // wave; they run in a loop without masking code, the few others (causal
+    // diagonal, ragged tail) in a second loop.  Unrolling by the stage
+    // count keeps buffer indices literal.
+    const int nplain = max(min(nfull, nkt) - 1, 0);
+    int j = 0;
+    for (; j + kStages <= nplain; j += kStages) {
+#pragma unroll
+      for (int u = 0; u < kStages; ++u) round(j + u, u, false, LEAD);
+    }
+    for (; j < nkt; j += kStages) {
+      round(j, 0, true, LEAD);
+#pragma unroll
+      for (int u = 1; u < kStages; ++u)
+        if (j + u < nkt) round(j + u, u, true, LEAD);
+    }
+    if (LEAD) lds_barrier();  // the trailing group's last barrier
+    wait_vmem_all();          // the zero-filling loads past the end
   };
 
   if (nkt > 0) {
-    issue_k(0, 0);
-    issue_v(0, 0);
-    if (nkt > 1) issue_k(1, 1);
-    wait_vmem_all();
-    __syncthreads();
-    scores(sreg[0], 0);
-    if (0 >= nfull) mask(sreg[0], 0);
-    {
-      float mx[QB];
-      rowmax(sreg[0], mx);
-      raise_ref(mx);
-    }
-    wait_vmem_all();
-    __syncthreads();
-    int j = 0;
-    for (; j + 2 < nkt; j += 2) {
-      step(j, 0);
-      step(j + 1, 1);
-    }
-    if (j + 1 < nkt) {
-      step(j, 0);
-      last(1);
-    } else {
-      last(0);
-    }
+    if (lead)
+      run(true);
+    else
+      run(false);
   }
 
   // ---- epilogue: one normalised write per row
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = wq0 + 32 * qb + n;
-    const float lt = sum_halves(l_run[qb]);
-    const float lr = sum_halves(l_rnd[qb]);
+  {
+    const int qrow = wq0 + n;
+    const float lt = sum_halves(l_run);
+    const float lr = ATTN_FWD_MFMA_LSUM ? acc_l[0] : sum_halves(l_rnd);
     if (qrow < a.Sq) {
       const float inv = lr > 0.f ? 1.f / lr : 0.f;
       uint16_t* O = a.o + ((size_t)(b * a.H + hq) * a.Sq + qrow) * D;
@@ -439,13 +489,12 @@ __global__ void __launch_bounds__(kThreads, kMinBlocks) fwd_bf16_kernel(FwdKerne
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
           // registers 4*rg .. 4*rg+3: head dims 32*db + 8*rg + 4*h + 0..3
-          const uint32_t w0 = pack_bf16x2(acc_o[qb][db][4 * rg + 0] * inv, acc_o[qb][db][4 * rg + 1] * inv);
-          const uint32_t w1 = pack_bf16x2(acc_o[qb][db][4 * rg + 2] * inv, acc_o[qb][db][4 * rg + 3] * inv);
+          const uint32_t w0 = pack_bf16x2(acc_o[db][4 * rg + 0] * inv, acc_o[db][4 * rg + 1] * inv);
+          const uint32_t w1 = pack_bf16x2(acc_o[db][4 * rg + 2] * inv, acc_o[db][4 * rg + 3] * inv);
           *reinterpret_cast<u32x2*>(O + 32 * db + 8 * rg + 4 * h) = u32x2{w0, w1};
         }
       if (a.lse != nullptr && h == 0) {
-        a.lse[(size_t)(b * a.H + hq) * a.Sq + qrow] =
-            lt > 0.f ? (m_ref[qb] + fast_log2(lt)) * kLn2 : -INFINITY;
+        a.lse[(size_t)(b * a.H + hq) * a.Sq + qrow] = lt > 0.f ? (m_ref + fast_log2(lt)) * kLn2 : -INFINITY;
       }
     }
   }

@@ -3,8 +3,9 @@
 Argument marshalling only: torch tensors supply device memory and the current
 stream, every step of the computation runs in the library's HIP kernels.  The
 raw entry points keep the C names (``attn_fwd``, ``attn_verify``,
-``attn_verify_workspace_bytes``, ``attn_strerror``); ``fwd`` and ``verify``
-are tensor-level conveniences over them.  Importing this module raises if the
+``attn_verify_paged``, ``attn_verify_workspace_bytes``, ``attn_strerror``);
+``fwd``, ``verify`` and ``verify_paged`` are tensor-level conveniences over
+them.  Importing this module raises if the
 library has not been built: there is no fallback path.
 """
 from __future__ import annotations
@@ -40,10 +41,13 @@ lib.attn_verify_workspace_bytes.restype = _sz
 lib.attn_verify_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]  # B, H, Hkv, kq, d
 lib.attn_verify.restype = _i
 lib.attn_verify.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]
+lib.attn_verify_paged.restype = _i
+lib.attn_verify_paged.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,
+                                  _vp, _sz, _vp]
 lib.attn_strerror.restype = ctypes.c_char_p
 lib.attn_strerror.argtypes = [_i]
 
-EXPORTED = ("attn_fwd", "attn_verify", "attn_verify_workspace_bytes", "attn_strerror")
+EXPORTED = ("attn_fwd", "attn_verify", "attn_verify_paged", "attn_verify_workspace_bytes", "attn_strerror")
 
 
 class AttnError(RuntimeError):
@@ -70,6 +74,15 @@ def attn_verify(q, k_cache, v_cache, seqlens_k, max_seqlen_k, cache_stride, o, l
     """Raw C entry point (device pointers as ints); returns the ATTN_* code."""
     return lib.attn_verify(q, k_cache, v_cache, seqlens_k, max_seqlen_k, cache_stride, o, lse, B, H, Hkv,
                            kq, d, float(scale), dtype, workspace, workspace_bytes, stream)
+
+
+def attn_verify_paged(q, k_pages, v_pages, block_table, max_blocks_per_seq, num_pages, page_size, seqlens_k,
+                      max_seqlen_k, o, lse, B, H, Hkv, kq, d, scale, dtype, workspace, workspace_bytes,
+                      stream) -> int:
+    """Raw C entry point (device pointers as ints); returns the ATTN_* code."""
+    return lib.attn_verify_paged(q, k_pages, v_pages, block_table, max_blocks_per_seq, num_pages, page_size,
+                                 seqlens_k, max_seqlen_k, o, lse, B, H, Hkv, kq, d, float(scale), dtype,
+                                 workspace, workspace_bytes, stream)
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -136,4 +149,32 @@ def verify(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seqlen
                      _ptr(workspace), workspace.numel(), _stream(q))
     if rc != ATTN_OK:
         raise AttnError(rc, "attn_verify")
+    return out, lse
+
+
+def verify_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
+                 seqlens_k: torch.Tensor, max_seqlen_k: int, scale: Optional[float] = None,
+                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None,
+                 want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """O, LSE of q [B,H,kq,d] against pages [num_pages,Hkv,page_size,d] through an int32
+    block table [B, max_blocks] with int32 seqlens_k [B]."""
+    B, H, kq, d = q.shape
+    num_pages, Hkv, page_size = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, kq), dtype=torch.float32, device=q.device)
+    need = attn_verify_workspace_bytes(B, H, Hkv, kq, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if seqlens_k.dtype != torch.int32 or block_table.dtype != torch.int32:
+        raise TypeError("seqlens_k and block_table must be int32")
+    rc = attn_verify_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), block_table.shape[1],
+                           num_pages, page_size, _ptr(seqlens_k), max_seqlen_k, _ptr(out), _ptr(lse),
+                           B, H, Hkv, kq, d, scale, _dtype_code(q), _ptr(workspace), workspace.numel(), _stream(q))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_verify_paged")
     return out, lse

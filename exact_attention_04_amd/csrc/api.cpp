@@ -90,6 +90,11 @@ extern "C" int attn_verify(const void* q, const void* k_cache, const void* v_cac
   a.k = k_cache;
   a.v = v_cache;
   a.seqlens = seqlens_k;
+  a.paged = false;
+  a.block_table = nullptr;
+  a.max_blocks = 0;
+  a.num_pages = 0;
+  a.page_shift = 0;
   a.o = o;
   a.lse = lse;
   a.B = B;
@@ -99,6 +104,62 @@ extern "C" int attn_verify(const void* q, const void* k_cache, const void* v_cac
   a.d = d;
   a.max_seqlen_k = max_seqlen_k;
   a.cache_stride = cache_stride;
+  a.scale = scale;
+  a.workspace = workspace;
+  const hipError_t e = attn::launch_verify_bf16(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+extern "C" int attn_verify_paged(const void* q, const void* k_pages, const void* v_pages,
+                                 const int32_t* block_table, int max_blocks_per_seq, int num_pages,
+                                 int page_size, const int32_t* seqlens_k, int max_seqlen_k,
+                                 void* o, float* lse, int B, int H, int Hkv, int kq, int d,
+                                 float scale, int dtype, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (B < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || kq < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
+  if (max_seqlen_k < 0 || max_blocks_per_seq < 0 || num_pages < 0) return ATTN_ERR_INVALID_ARG;
+  int page_shift = 0;
+  while (page_shift < 13 && (1 << page_shift) != page_size) ++page_shift;
+  if (page_size < 32 || page_size > 4096 || (1 << page_shift) != page_size) return ATTN_ERR_INVALID_ARG;
+  if ((long long)max_seqlen_k > (long long)max_blocks_per_seq * page_size) return ATTN_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if ((H / Hkv) * kq > 32) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)B * max_seqlen_k >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;  // total keys fit int32
+  const size_t nq = (size_t)B * H * kq * d;
+  const size_t nk = (size_t)num_pages * Hkv * page_size * d;
+  const size_t nt = (size_t)B * max_blocks_per_seq;
+  if (nq > kMaxElems || nk > kMaxElems || nt > kMaxElems) return ATTN_ERR_INVALID_ARG;
+  if (!ptr_ok(q, nq) || !ptr_ok(o, nq) || !ptr_ok(k_pages, nk) || !ptr_ok(v_pages, nk))
+    return ATTN_ERR_INVALID_ARG;
+  if (B > 0 && (seqlens_k == nullptr || !aligned4(seqlens_k))) return ATTN_ERR_INVALID_ARG;
+  if (max_seqlen_k > 0 && (block_table == nullptr || !aligned4(block_table))) return ATTN_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned4(lse)) return ATTN_ERR_INVALID_ARG;
+  const size_t need = attn::verify_workspace_bytes(B, H, Hkv, kq, d);
+  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (need > 0 && (workspace == nullptr || !aligned16(workspace))) return ATTN_ERR_INVALID_ARG;
+  if (nq == 0) return ATTN_OK;
+
+  attn::VerifyArgs a;
+  a.q = q;
+  a.k = k_pages;
+  a.v = v_pages;
+  a.seqlens = seqlens_k;
+  a.paged = true;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_pages = num_pages;
+  a.page_shift = page_shift;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.kq = kq;
+  a.d = d;
+  a.max_seqlen_k = max_seqlen_k;
+  a.cache_stride = 0;
   a.scale = scale;
   a.workspace = workspace;
   const hipError_t e = attn::launch_verify_bf16(a, static_cast<hipStream_t>(stream));

@@ -23,6 +23,9 @@ struct VerifyArgs {
   const void* k;
   const void* v;
   const int32_t* seqlens;
+  bool paged;                  // false: contiguous cache [B][Hkv][cache_stride][d]
+  const int32_t* block_table;  // paged: [B][max_blocks], pages [num_pages][Hkv][2^page_shift][d]
+  int max_blocks, num_pages, page_shift;
   void* o;
   float* lse;  // may be null
   int B, H, Hkv, kq, d;

@@ -26,6 +26,15 @@
 //     two denominators (fp32 for LSE, bf16-rounded for O);
 //   * the waves' (m, l, O) are combined through LDS into one fp32 partial
 //     (O normalised, base-2 LSE) per packed row.
+// Piece boundaries inside a segment fall on multiples of 32 keys, so every
+// wave step is 32 consecutive keys starting at a multiple of 32.  That lets
+// the same kernel read a paged cache ("Warmup Guide", Ch.8: fixed-size
+// blocks of tokens, a per-sequence block table from logical to physical
+// block): with a page size that is a multiple of 32, a step lies inside one
+// page, so the table is consulted once per step and each step's loads use
+// one buffer descriptor, as for the contiguous cache.  A wave keeps 64
+// consecutive table entries of its sequence in a VGPR (one per lane) and
+// picks a step's entry with readlane.
 // Merge kernel -- one wave per output row combines its segment's piece
 // partials (weights exp(LSE_p - LSE)) and writes O (bf16) and LSE (natural
 // log).
@@ -49,9 +58,11 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units
 
 struct SplitArgs {
   const uint16_t* q;
-  const uint16_t* k;
+  const uint16_t* k;  // contiguous: [B][Hkv][cache_stride][D]; paged: [num_pages][Hkv][page][D]
   const uint16_t* v;
   const int32_t* seqlens;
+  const int32_t* block_table;  // paged only: [B][max_blocks]
+  int max_blocks, num_pages, page_shift;
   float* part_o;    // [B][Hkv][jmax][R][D]
   float* part_lse;  // [B][Hkv][jmax][R]   base-2 domain: m2 + log2(l)
   int32_t* seg_np;  // [B][Hkv]  pieces of each non-empty segment
@@ -106,7 +117,7 @@ __device__ __forceinline__ void slice_plan(const int32_t* seqlens, int B, int Hk
   T = (total + kSplitWgs - 1) / kSplitWgs;
 }
 
-template <int D>
+template <int D, bool PAGED>
 __global__ void __launch_bounds__(kThreads, 1) verify_split_kernel(SplitArgs a) {
   constexpr int KS = D / 16;
   constexpr int NDB = D / 32;
@@ -184,14 +195,46 @@ __global__ void __launch_bounds__(kThreads, 1) verify_split_kernel(SplitArgs a) 
       for (int ks = 0; ks < KS; ++ks) qf[ks] = row_ok ? load16(qrow + ks * 16 + h * 8) : u32x4{0, 0, 0, 0};
     }
 
-    // A step's buffer starts at its first key and ends at k1: rows past the
-    // piece read as zero, and a step past the end reads nothing.
+    // Paged cache: the wave's window of 64 block-table entries of sequence b
+    // (lane i holds logical page win0 + i; -1 past the table).
+    int win0 = 0, win = -1;
+    auto load_window = [&](int page) {
+      wait_vmem_all();  // keeps the counted waits of the step loop exact
+      win0 = page;
+      const int lp = page + lane;
+      win = lp < a.max_blocks ? a.block_table[(size_t)b * a.max_blocks + lp] : -1;
+      wait_vmem_all();
+    };
+    // A step's buffer starts at its first key and ends at k1 (at most one
+    // step): rows past the piece read as zero, and a step past the end reads
+    // nothing.  In a paged cache the step's rows are rows key0 % page.. of
+    // physical page table[key0 / page]; an entry outside [0, num_pages)
+    // reads as zeros.
     auto issue = [&](int key0, const int ST) {
-      const int bytes = max(k1 - key0, 0) * D * 2;
+      int bytes = max(min(k1 - key0, kStep), 0) * D * 2;
+      const uint16_t* kbase;
+      const uint16_t* vbase;
+      if constexpr (PAGED) {
+        size_t off = 0;
+        if (bytes > 0) {
+          const int page = key0 >> a.page_shift;
+          if (page < win0 || page >= win0 + 64) load_window(page);
+          const int phys = __builtin_amdgcn_readlane(win, page - win0);
+          if ((unsigned)phys < (unsigned)a.num_pages)
+            off = (((size_t)phys * a.Hkv + g) << a.page_shift) + (key0 & ((1 << a.page_shift) - 1));
+          else
+            bytes = 0;
+        }
+        kbase = a.k + off * D;
+        vbase = a.v + off * D;
+      } else {
+        kbase = Kb + (size_t)key0 * D;
+        vbase = Vb + (size_t)key0 * D;
+      }
       const __amdgpu_buffer_rsrc_t kr =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(Kb + (size_t)key0 * D), (short)0, bytes, kBufferWord3);
+          __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, bytes, kBufferWord3);
       const __amdgpu_buffer_rsrc_t vr =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(Vb + (size_t)key0 * D), (short)0, bytes, kBufferWord3);
+          __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, bytes, kBufferWord3);
       uint16_t* kd = ST ? k_st1[wave] : k_st0[wave];
       uint16_t* vd = ST ? v_st1[wave] : v_st0[wave];
 #pragma unroll
@@ -273,6 +316,7 @@ __global__ void __launch_bounds__(kThreads, 1) verify_split_kernel(SplitArgs a) 
     // is exact.
     const int first = k0 + kStep * wave;
     const int nsteps = first < k1 ? (k1 - first + kStep * kWaves - 1) / (kStep * kWaves) : 0;
+    if (PAGED && nsteps > 0) load_window(first >> a.page_shift);
     auto step = [&](int i, const int ST) {
       const int key0 = first + kStep * kWaves * i;
       issue(key0 + kStep * kWaves, ST ^ 1);
@@ -364,7 +408,12 @@ __global__ void __launch_bounds__(kThreads, 1) verify_split_kernel(SplitArgs a) 
           if (k0 < k1) {
             const int j = (int)((c0 + k0) / T - c0 / T);
             if (j == 0 && tid == 0) a.seg_np[b * a.Hkv + g] = (int)(1 + (c0 + sk - 1) / T - c0 / T);
-            piece(b, g, sk, (int)k0, (int)k1, j);
+            // boundaries between pieces move down to a multiple of 32 (the
+            // neighbouring piece rounds the same boundary the same way); a
+            // piece left empty still writes its (empty) partial
+            const int k0r = (int)k0 & ~(kStep - 1);
+            const int k1r = k1 == sk ? sk : ((int)k1 & ~(kStep - 1));
+            piece(b, g, sk, k0r, k1r, j);
           }
         }
       }
@@ -480,7 +529,7 @@ __global__ void __launch_bounds__(256) verify_merge_kernel(MergeArgs a) {
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
-template <int D>
+template <int D, bool PAGED>
 hipError_t launch(const VerifyArgs& p, hipStream_t s) {
   const int G = p.H / p.Hkv;
   const int R = G * p.kq;
@@ -496,6 +545,10 @@ hipError_t launch(const VerifyArgs& p, hipStream_t s) {
   sa.k = static_cast<const uint16_t*>(p.k);
   sa.v = static_cast<const uint16_t*>(p.v);
   sa.seqlens = p.seqlens;
+  sa.block_table = p.block_table;
+  sa.max_blocks = p.max_blocks;
+  sa.num_pages = p.num_pages;
+  sa.page_shift = p.page_shift;
   sa.part_o = part_o;
   sa.part_lse = part_lse;
   sa.seg_np = seg_np;
@@ -510,7 +563,7 @@ hipError_t launch(const VerifyArgs& p, hipStream_t s) {
   sa.jmax = jmax;
   sa.c2 = p.scale * kLog2e;
   if (p.max_seqlen_k > 0) {
-    hipLaunchKernelGGL((verify_split_kernel<D>), dim3(kSplitWgs), dim3(kThreads), 0, s, sa);
+    hipLaunchKernelGGL((verify_split_kernel<D, PAGED>), dim3(kSplitWgs), dim3(kThreads), 0, s, sa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -546,7 +599,8 @@ size_t verify_workspace_bytes(int B, int H, int Hkv, int kq, int d) {
 }
 
 hipError_t launch_verify_bf16(const VerifyArgs& p, hipStream_t s) {
-  return p.d == 128 ? launch<128>(p, s) : launch<64>(p, s);
+  if (p.paged) return p.d == 128 ? launch<128, true>(p, s) : launch<64, true>(p, s);
+  return p.d == 128 ? launch<128, false>(p, s) : launch<64, false>(p, s);
 }
 
 }  // namespace attn

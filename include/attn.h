@@ -117,6 +117,38 @@ int attn_verify(const void* q, const void* k_cache, const void* v_cache,
                 float scale, int dtype, void* workspace, size_t workspace_bytes,
                 void* stream);
 
+/*
+ * attn_verify_paged -- attn_verify on a paged KV cache ("Warmup Guide --
+ * Inference Optimization at Depth", Ch.8: the cache is stored in fixed-size
+ * blocks of tokens and each sequence owns a block table mapping its logical
+ * blocks to physical ones; the attention kernel gathers K/V through the table,
+ * once per tile, as the guide's interview answer on FlashAttention and
+ * PagedAttention describes).  Same queries, outputs, masking, workspace and
+ * semantics as attn_verify; only the cache addressing differs:
+ *
+ *   k_pages, v_pages  [num_pages, Hkv, page_size, d]  bf16 (read)
+ *   block_table       [B, max_blocks_per_seq] int32 (device): logical block i
+ *                     of sequence b (its keys i*page_size .. +page_size-1) is
+ *                     physical page block_table[b][i].  Pages may be shared
+ *                     between sequences (prefix sharing).  Only the entries
+ *                     covering seqlens_k[b] keys are read; an entry outside
+ *                     [0, num_pages) reads as zero keys and values.
+ *   page_size         keys per page: a power of two in [32, 4096] (a multiple
+ *                     of the kernel's 32-key step, so each step reads one
+ *                     page)
+ *   max_seqlen_k      host bound, <= max_blocks_per_seq * page_size
+ *
+ * Workspace: attn_verify_workspace_bytes(B, H, Hkv, kq, d) bytes.  Errors as
+ * for attn_verify, plus ATTN_ERR_INVALID_ARG for a page size outside the
+ * supported set or a null block table when max_seqlen_k > 0.
+ */
+int attn_verify_paged(const void* q, const void* k_pages, const void* v_pages,
+                      const int32_t* block_table, int max_blocks_per_seq, int num_pages,
+                      int page_size, const int32_t* seqlens_k, int max_seqlen_k,
+                      void* o, float* lse, int B, int H, int Hkv, int kq, int d,
+                      float scale, int dtype, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
 /* Static, human-readable name of an ATTN_* return code. */
 const char* attn_strerror(int code);
 

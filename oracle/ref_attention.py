@@ -215,6 +215,47 @@ def verify(q, k_cache, v_cache, seqlens_k, scale: float,
     return out, lse
 
 
+def gather_paged(pages, block_table, seqlens_k, page_size: int) -> np.ndarray:
+    """The logical cache [B, Hkv, max_len, d] held by a paged store.
+
+    "Warmup Guide", Ch.8 (PagedAttention): KV storage is divided into
+    fixed-size blocks of ``page_size`` tokens and each sequence holds a block
+    table mapping its logical blocks to physical ones.  Logical key t of
+    sequence b is therefore row t % page_size of physical page
+    block_table[b][t // page_size].  pages: [num_pages, Hkv, page_size, d].
+    Rows at or past seqlens_k[b] are zero, and so are the rows of a block
+    whose table entry is not a valid page index (the library reads such a
+    block as zeros).
+    """
+    pages = np.asarray(pages, dtype=np.float64)
+    table = np.asarray(block_table)
+    sl = [int(x) for x in np.asarray(seqlens_k).reshape(-1)]
+    num_pages, Hkv, ps, d = pages.shape
+    if ps != page_size:
+        raise ValueError("pages must be [num_pages, Hkv, page_size, d]")
+    B = len(sl)
+    max_len = max(sl) if sl else 0
+    out = np.zeros((B, Hkv, max_len, d), dtype=np.float64)
+    for b in range(B):
+        for blk in range((sl[b] + page_size - 1) // page_size):
+            phys = int(table[b, blk])
+            t0 = blk * page_size
+            n = min(page_size, sl[b] - t0)
+            if 0 <= phys < num_pages:
+                out[b, :, t0:t0 + n] = pages[phys, :, :n]
+    return out
+
+
+def verify_paged(q, k_pages, v_pages, block_table, seqlens_k, page_size: int, scale: float,
+                 heads: Optional[Sequence[Tuple[int, int]]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Speculative-verify attention over a paged KV cache: the logical cache
+    of ``gather_paged`` fed to ``verify`` (paging changes where K/V live,
+    not what attention computes)."""
+    k = gather_paged(k_pages, block_table, seqlens_k, page_size)
+    v = gather_paged(v_pages, block_table, seqlens_k, page_size)
+    return verify(q, k, v, seqlens_k, scale, heads=heads)
+
+
 def online_softmax_1d(x: Sequence[float], blocks: Iterable[int]) -> Tuple[float, float]:
     """Streaming (m, l) over the blocks of a 1-D score vector.
 

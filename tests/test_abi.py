@@ -136,3 +136,47 @@ def test_verify_workspace_formula():
 
 def test_verify_empty_batch_is_a_noop():
     assert call_verify(B=0, q=None, o=None, sl=None, k=None, v=None, ws=None, maxs=0, stride=0) == bd.ATTN_OK
+
+
+def paged_args(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, table=FAKE, maxb=100, npages=400, page=64, sl=FAKE, maxs=3000, o=FAKE,
+             lse=FAKE, B=2, H=32, Hkv=8, kq=5, d=128, scale=0.088, dtype=bd.ATTN_BF16, ws=FAKE, wsb=None,
+             stream=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = bd.attn_verify_workspace_bytes(a["B"], a["H"], a["Hkv"], a["kq"], 128)
+    return a
+
+
+def call_paged(**kw):
+    a = paged_args(**kw)
+    return bd.attn_verify_paged(a["q"], a["k"], a["v"], a["table"], a["maxb"], a["npages"], a["page"], a["sl"],
+                                a["maxs"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["kq"], a["d"],
+                                a["scale"], a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(table=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(table=FAKE + 2), bd.ATTN_ERR_INVALID_ARG),
+    (dict(page=16), bd.ATTN_ERR_INVALID_ARG),       # below the 32-key step
+    (dict(page=48), bd.ATTN_ERR_INVALID_ARG),       # not a power of two
+    (dict(page=8192), bd.ATTN_ERR_INVALID_ARG),
+    (dict(maxs=6401), bd.ATTN_ERR_INVALID_ARG),     # more keys than the table covers (100 * 64)
+    (dict(maxb=-1), bd.ATTN_ERR_INVALID_ARG),
+    (dict(npages=-1), bd.ATTN_ERR_INVALID_ARG),
+    (dict(k=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(sl=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(H=30), bd.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), bd.ATTN_ERR_INVALID_ARG),
+    (dict(dtype=bd.ATTN_F32), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(d=96), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(kq=9), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(wsb=100), bd.ATTN_ERR_WORKSPACE),
+])
+def test_verify_paged_rejects(kw, code):
+    assert call_paged(**kw) == code
+
+
+def test_verify_paged_empty_batch_is_a_noop():
+    assert call_paged(B=0, q=None, o=None, sl=None, table=None, k=None, v=None, ws=None, maxs=0,
+                      npages=0) == bd.ATTN_OK

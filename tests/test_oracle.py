@@ -434,3 +434,61 @@ def test_synth_is_seeded_and_rounded():
     assert np.all(sl.numpy() == L + 5)
     assert k.shape == (8, 8, int(sl.max()), 128)
     assert L.min() >= 1024 and L.max() <= 16384
+
+
+# ---------------------------------------------------------------- paged cache
+def test_gather_paged_hand_example():
+    """"Warmup Guide", Ch.8: logical key t of sequence b is row t % page of
+    page table[b][t // page].  Pages of 2 tokens whose entries name their own
+    (page, row); sequence 0 uses pages 2 then 0, sequence 1 shares page 1 for
+    both of its blocks (prefix sharing), sequence 2 has an invalid entry."""
+    page, npg = 2, 3
+    pages = np.zeros((npg, 1, page, 2))
+    for p in range(npg):
+        for r in range(page):
+            pages[p, 0, r] = [p, r]
+    table = np.array([[2, 0], [1, 1], [-1, 7]])
+    sl = [3, 4, 2]
+    got = ref.gather_paged(pages, table, sl, page)
+    expect0 = [[2, 0], [2, 1], [0, 0]]            # page 2 rows 0,1, then page 0 row 0
+    expect1 = [[1, 0], [1, 1], [1, 0], [1, 1]]    # page 1 twice
+    np.testing.assert_array_equal(got[0, 0, :3], expect0)
+    np.testing.assert_array_equal(got[0, 0, 3:], 0)  # past the length
+    np.testing.assert_array_equal(got[1, 0], expect1)
+    np.testing.assert_array_equal(got[2], 0)  # invalid page index reads as zeros
+
+
+@pytest.mark.parametrize("page", [1, 4, 32])
+def test_verify_paged_equals_contiguous_under_any_page_permutation(page):
+    """Paging changes where K/V live, not the result: scatter a contiguous
+    cache into randomly permuted pages (with spare pages full of NaN that no
+    table entry names) and the paged oracle must give the contiguous result
+    exactly."""
+    rng = np.random.default_rng(11)
+    B, H, Hkv, kq, d = 3, 4, 2, 3, 8
+    sl = np.array([37, 5, 64])
+    smax = int(sl.max())
+    q = rng.standard_normal((B, H, kq, d))
+    k = rng.standard_normal((B, Hkv, smax, d))
+    v = rng.standard_normal((B, Hkv, smax, d))
+    nblk = (sl + page - 1) // page
+    total = int(nblk.sum())
+    perm = rng.permutation(total + 5)  # 5 spare pages
+    kp = np.full((total + 5, Hkv, page, d), np.nan)
+    vp = np.full((total + 5, Hkv, page, d), np.nan)
+    table = np.full((B, int(nblk.max())), -1)
+    i = 0
+    for b in range(B):
+        for blk in range(nblk[b]):
+            phys = perm[i]
+            i += 1
+            table[b, blk] = phys
+            n = min(page, sl[b] - blk * page)
+            kp[phys] = 0.0
+            vp[phys] = 0.0
+            kp[phys, :, :n] = k[b, :, blk * page:blk * page + n]
+            vp[phys, :, :n] = v[b, :, blk * page:blk * page + n]
+    o_c, l_c = ref.verify(q, k, v, sl, 0.4)
+    o_p, l_p = ref.verify_paged(q, kp, vp, table, sl, page, 0.4)
+    np.testing.assert_array_equal(o_p, o_c)
+    np.testing.assert_array_equal(l_p, l_c)

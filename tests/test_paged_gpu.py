@@ -1,0 +1,141 @@
+"""GPU parity of attn_verify_paged (verify over a paged KV cache) against the
+CPU fp64 oracle, and its bitwise agreement with attn_verify on the same
+logical cache.
+
+The paged layout follows "Warmup Guide -- Inference Optimization at Depth",
+Ch.8: fixed-size pages of tokens, a per-sequence block table from logical to
+physical pages, pages shared between sequences for common prefixes.
+"""
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_04_amd import synth
+from oracle import ref_attention as ref
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    from exact_attention_04_amd import binding
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return binding
+
+
+def to_pages(k, v, sl, page, rng, spare=3, shared_prefix_blocks=0):
+    """Scatter contiguous caches [B, Hkv, S, d] (device) into randomly
+    permuted pages [num_pages, Hkv, page, d].  Every row that no (sequence,
+    key < seqlen) pair maps to -- spare pages, the tail of a last page -- is
+    NaN, so an over-read poisons the result.  With shared_prefix_blocks = n,
+    every sequence's first n blocks are sequence 0's pages (its prefix is
+    copied over first, so the logical caches agree)."""
+    B, Hkv, S, d = k.shape
+    sl = [int(x) for x in sl]
+    nblk = [(s + page - 1) // page for s in sl]
+    own = [max(nb - (shared_prefix_blocks if b > 0 else 0), 0) for b, nb in enumerate(nblk)]
+    total = sum(own)
+    perm = rng.permutation(total + spare)
+    kp = torch.full((total + spare, Hkv, page, d), float("nan"), dtype=k.dtype, device=k.device)
+    vp = torch.full_like(kp, float("nan"))
+    table = np.full((B, max(max(nblk), 1)), -1, dtype=np.int32)
+    i = 0
+    for b in range(B):
+        for blk in range(nblk[b]):
+            if b > 0 and blk < shared_prefix_blocks:
+                table[b, blk] = table[0, blk]
+                continue
+            phys = int(perm[i])
+            i += 1
+            table[b, blk] = phys
+            n = min(page, sl[b] - blk * page)
+            kp[phys, :, :n] = k[b, :, blk * page:blk * page + n]
+            vp[phys, :, :n] = v[b, :, blk * page:blk * page + n]
+    return kp, vp, table
+
+
+def run_paged(q, kp, vp, table, sl, scale):
+    from exact_attention_04_amd import binding
+    o, lse = binding.verify_paged(q, kp, vp, torch.from_numpy(table).cuda(), torch.from_numpy(sl).cuda(),
+                                  int(sl.max()) if len(sl) else 0, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check_paged(q, kp, vp, table, sl, page, o, lse, scale, what):
+    o_ref, l_ref = ref.verify_paged(synth.to_f64(q), synth.to_f64(kp), synth.to_f64(vp), table, sl, page, scale)
+    res = P.compare(synth.to_f64(o), synth.to_f64(lse), o_ref, l_ref, "bf16", what)
+    P.log(f"    ok {res}")
+    return res
+
+
+def paged_case(seed, lengths, H, Hkv, kq, d, page, shared=0, what=""):
+    rng = np.random.default_rng(seed)
+    B = len(lengths)
+    sl = np.asarray(lengths, dtype=np.int32)
+    smax = max(1, int(sl.max()))
+    q = synth.normal(rng, (B, H, kq, d), "bf16").cuda()
+    k = synth.normal(rng, (B, Hkv, smax, d), "bf16").cuda()
+    v = synth.normal(rng, (B, Hkv, smax, d), "bf16").cuda()
+    if shared:
+        n = min(shared * page, smax)
+        for b in range(1, B):
+            k[b, :, :n] = k[0, :, :n]
+            v[b, :, :n] = v[0, :, :n]
+    kp, vp, table = to_pages(k, v, sl, page, rng, shared_prefix_blocks=shared)
+    scale = float(np.float32(d ** -0.5))
+    P.log(f"[paged] {what} seed={seed} lengths={lengths} H={H} Hkv={Hkv} kq={kq} d={d} page={page} shared={shared}")
+    o, lse = run_paged(q, kp, vp, table, sl, scale)
+    return check_paged(q, kp, vp, table, sl, page, o, lse, scale, what)
+
+
+@pytest.mark.parametrize("page", [32, 64, 256])
+@pytest.mark.parametrize("d", [64, 128])
+def test_paged_matches_oracle(page, d):
+    paged_case(page + d, [1000, 37, 5, 2500, 64, 33], 16, 4, 5, d, page, what="ragged")
+
+
+@pytest.mark.parametrize("page", [32, 128])
+def test_paged_prefix_sharing(page):
+    """Sequences whose first blocks are the same physical pages."""
+    paged_case(7, [700, 900, 513, 1300], 32, 8, 5, 128, page, shared=3, what="prefix-sharing")
+
+
+def test_paged_short_and_empty():
+    paged_case(3, [0, 1, 4, 5, 6, 31, 32, 33], 8, 2, 5, 128, 32, what="short")
+
+
+def test_paged_invalid_entries_read_zero():
+    """Table entries outside [0, num_pages) read as zero keys and values."""
+    rng = np.random.default_rng(5)
+    B, H, Hkv, kq, d, page = 2, 8, 2, 5, 128, 64
+    sl = np.array([300, 200], dtype=np.int32)
+    q = synth.normal(rng, (B, H, kq, d), "bf16").cuda()
+    k = synth.normal(rng, (B, Hkv, 300, d), "bf16").cuda()
+    v = synth.normal(rng, (B, Hkv, 300, d), "bf16").cuda()
+    kp, vp, table = to_pages(k, v, sl, page, rng, spare=0)
+    table[0, 1] = -1
+    table[1, 0] = kp.shape[0] + 10
+    scale = float(np.float32(d ** -0.5))
+    P.log(f"[paged] invalid entries table={table.tolist()}")
+    o, lse = run_paged(q, kp, vp, table, sl, scale)
+    check_paged(q, kp, vp, table, sl, page, o, lse, scale, "invalid-entries")
+
+
+@pytest.mark.parametrize("page", [64, 1024])
+def test_paged_full_workload_bitwise_equals_contiguous(page):
+    """Seed-4 verify workload: the paged call over randomly permuted pages gives
+    bit-identical O and LSE to the contiguous call (same logical cache, same
+    arithmetic order), and matches the oracle."""
+    from exact_attention_04_amd import binding
+    w = synth.VERIFY_BF16
+    q, k, v, sl = synth.verify_inputs(w, "cuda")
+    sl_h = sl.cpu().numpy()
+    P.log(f"[paged] {w.name} page={page} lengths={sl_h.tolist()}")
+    o_c, l_c = binding.verify(q, k, v, sl, int(sl_h.max()), scale=w.scale)
+    kp, vp, table = to_pages(k, v, sl_h, page, np.random.default_rng(40 + page))
+    o_p, l_p = run_paged(q, kp, vp, table, sl_h, w.scale)
+    assert torch.equal(o_p, o_c)
+    assert torch.equal(l_p, l_c)
+    check_paged(q, kp, vp, table, sl_h, page, o_p, l_p, w.scale, w.name)

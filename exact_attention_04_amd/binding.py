@@ -3,9 +3,9 @@
 Argument marshalling only: torch tensors supply device memory and the current
 stream, every step of the computation runs in the library's HIP kernels.  The
 raw entry points keep the C names (``attn_fwd``, ``attn_verify``,
-``attn_verify_paged``, ``attn_verify_workspace_bytes``, ``attn_strerror``);
-``fwd``, ``verify`` and ``verify_paged`` are tensor-level conveniences over
-them.  Importing this module raises if the
+``attn_verify_tree``, ``attn_verify_paged``, ``attn_verify_workspace_bytes``,
+``attn_strerror``); ``fwd``, ``verify``, ``verify_tree`` and ``verify_paged``
+are tensor-level conveniences over them.  Importing this module raises if the
 library has not been built: there is no fallback path.
 """
 from __future__ import annotations
@@ -41,13 +41,17 @@ lib.attn_verify_workspace_bytes.restype = _sz
 lib.attn_verify_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]  # B, H, Hkv, kq, d
 lib.attn_verify.restype = _i
 lib.attn_verify.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]
+lib.attn_verify_tree.restype = _i
+lib.attn_verify_tree.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz,
+                                 _vp]
 lib.attn_verify_paged.restype = _i
 lib.attn_verify_paged.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,
                                   _vp, _sz, _vp]
 lib.attn_strerror.restype = ctypes.c_char_p
 lib.attn_strerror.argtypes = [_i]
 
-EXPORTED = ("attn_fwd", "attn_verify", "attn_verify_paged", "attn_verify_workspace_bytes", "attn_strerror")
+EXPORTED = ("attn_fwd", "attn_verify", "attn_verify_tree", "attn_verify_paged", "attn_verify_workspace_bytes",
+            "attn_strerror")
 
 
 class AttnError(RuntimeError):
@@ -74,6 +78,13 @@ def attn_verify(q, k_cache, v_cache, seqlens_k, max_seqlen_k, cache_stride, o, l
     """Raw C entry point (device pointers as ints); returns the ATTN_* code."""
     return lib.attn_verify(q, k_cache, v_cache, seqlens_k, max_seqlen_k, cache_stride, o, lse, B, H, Hkv,
                            kq, d, float(scale), dtype, workspace, workspace_bytes, stream)
+
+
+def attn_verify_tree(q, k_cache, v_cache, seqlens_k, max_seqlen_k, cache_stride, tree_mask, o, lse, B, H, Hkv,
+                     kq, d, scale, dtype, workspace, workspace_bytes, stream) -> int:
+    """Raw C entry point (device pointers as ints); returns the ATTN_* code."""
+    return lib.attn_verify_tree(q, k_cache, v_cache, seqlens_k, max_seqlen_k, cache_stride, tree_mask, o, lse, B, H,
+                                Hkv, kq, d, float(scale), dtype, workspace, workspace_bytes, stream)
 
 
 def attn_verify_paged(q, k_pages, v_pages, block_table, max_blocks_per_seq, num_pages, page_size, seqlens_k,
@@ -177,4 +188,34 @@ def verify_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, 
                            B, H, Hkv, kq, d, scale, _dtype_code(q), _ptr(workspace), workspace.numel(), _stream(q))
     if rc != ATTN_OK:
         raise AttnError(rc, "attn_verify_paged")
+    return out, lse
+
+
+def verify_tree(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seqlens_k: torch.Tensor,
+                max_seqlen_k: int, tree_mask: torch.Tensor, scale: Optional[float] = None,
+                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None,
+                want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """verify() with the new tokens forming a draft tree: tree_mask [B, kq] (int32 or uint32 bits;
+    bit t of row i set iff node i sees new token t)."""
+    B, H, kq, d = q.shape
+    Hkv, stride = k_cache.shape[1], k_cache.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, kq), dtype=torch.float32, device=q.device)
+    need = attn_verify_workspace_bytes(B, H, Hkv, kq, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if seqlens_k.dtype != torch.int32 or tree_mask.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("seqlens_k must be int32 and tree_mask 32-bit")
+    if tuple(tree_mask.shape) != (B, kq):
+        raise ValueError("tree_mask must be [B, kq]")
+    rc = attn_verify_tree(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens_k), max_seqlen_k, stride,
+                          _ptr(tree_mask), _ptr(out), _ptr(lse), B, H, Hkv, kq, d, scale, _dtype_code(q),
+                          _ptr(workspace), workspace.numel(), _stream(q))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_verify_tree")
     return out, lse

@@ -61,11 +61,12 @@ extern "C" size_t attn_verify_workspace_bytes(int B, int H, int Hkv, int kq, int
   return attn::verify_workspace_bytes(B, H, Hkv, kq, d);
 }
 
-extern "C" int attn_verify(const void* q, const void* k_cache, const void* v_cache,
-                           const int32_t* seqlens_k, int max_seqlen_k, int cache_stride,
-                           void* o, float* lse, int B, int H, int Hkv, int kq, int d,
-                           float scale, int dtype, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+namespace {
+
+int verify_contiguous(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens_k,
+                      int max_seqlen_k, int cache_stride, const uint32_t* tree_mask, bool tree, void* o,
+                      float* lse, int B, int H, int Hkv, int kq, int d, float scale, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || kq < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
   if (max_seqlen_k < 0 || cache_stride < 0 || max_seqlen_k > cache_stride) return ATTN_ERR_INVALID_ARG;
   if (!scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
@@ -79,6 +80,7 @@ extern "C" int attn_verify(const void* q, const void* k_cache, const void* v_cac
   if (!ptr_ok(q, nq) || !ptr_ok(o, nq) || !ptr_ok(k_cache, nk) || !ptr_ok(v_cache, nk))
     return ATTN_ERR_INVALID_ARG;
   if (B > 0 && (seqlens_k == nullptr || !aligned4(seqlens_k))) return ATTN_ERR_INVALID_ARG;
+  if (tree && B > 0 && (tree_mask == nullptr || !aligned4(tree_mask))) return ATTN_ERR_INVALID_ARG;
   if (lse != nullptr && !aligned4(lse)) return ATTN_ERR_INVALID_ARG;
   const size_t need = attn::verify_workspace_bytes(B, H, Hkv, kq, d);
   if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
@@ -95,6 +97,7 @@ extern "C" int attn_verify(const void* q, const void* k_cache, const void* v_cac
   a.max_blocks = 0;
   a.num_pages = 0;
   a.page_shift = 0;
+  a.tree_mask = tree ? tree_mask : nullptr;
   a.o = o;
   a.lse = lse;
   a.B = B;
@@ -108,6 +111,26 @@ extern "C" int attn_verify(const void* q, const void* k_cache, const void* v_cac
   a.workspace = workspace;
   const hipError_t e = attn::launch_verify_bf16(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int attn_verify(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* seqlens_k, int max_seqlen_k, int cache_stride,
+                           void* o, float* lse, int B, int H, int Hkv, int kq, int d,
+                           float scale, int dtype, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return verify_contiguous(q, k_cache, v_cache, seqlens_k, max_seqlen_k, cache_stride, nullptr, false, o, lse,
+                           B, H, Hkv, kq, d, scale, dtype, workspace, workspace_bytes, stream);
+}
+
+extern "C" int attn_verify_tree(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* seqlens_k, int max_seqlen_k, int cache_stride,
+                                const uint32_t* tree_mask, void* o, float* lse, int B, int H, int Hkv,
+                                int kq, int d, float scale, int dtype, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return verify_contiguous(q, k_cache, v_cache, seqlens_k, max_seqlen_k, cache_stride, tree_mask, true, o, lse,
+                           B, H, Hkv, kq, d, scale, dtype, workspace, workspace_bytes, stream);
 }
 
 extern "C" int attn_verify_paged(const void* q, const void* k_pages, const void* v_pages,
@@ -148,6 +171,7 @@ extern "C" int attn_verify_paged(const void* q, const void* k_pages, const void*
   a.seqlens = seqlens_k;
   a.paged = true;
   a.block_table = block_table;
+  a.tree_mask = nullptr;
   a.max_blocks = max_blocks_per_seq;
   a.num_pages = num_pages;
   a.page_shift = page_shift;

@@ -26,6 +26,7 @@ struct VerifyArgs {
   bool paged;                  // false: contiguous cache [B][Hkv][cache_stride][d]
   const int32_t* block_table;  // paged: [B][max_blocks], pages [num_pages][Hkv][2^page_shift][d]
   int max_blocks, num_pages, page_shift;
+  const uint32_t* tree_mask;   // [B][kq] visibility bitmasks among the new tokens; null: causal chain
   void* o;
   float* lse;  // may be null
   int B, H, Hkv, kq, d;

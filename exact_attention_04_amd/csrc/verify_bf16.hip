@@ -63,6 +63,7 @@ struct SplitArgs {
   const int32_t* seqlens;
   const int32_t* block_table;  // paged only: [B][max_blocks]
   int max_blocks, num_pages, page_shift;
+  const uint32_t* tree_mask;   // [B][kq] ancestor bitmasks of the new tokens, or null (a chain)
   float* part_o;    // [B][Hkv][jmax][R][D]
   float* part_lse;  // [B][Hkv][jmax][R]   base-2 domain: m2 + log2(l)
   int32_t* seg_np;  // [B][Hkv]  pieces of each non-empty segment
@@ -184,7 +185,16 @@ __global__ void __launch_bounds__(kThreads, 1) verify_split_kernel(SplitArgs a) 
   // One piece: keys [k0, k1) of segment (b, g), whose length is sk; the
   // partial goes to slot j of the segment.
   auto piece = [&](int b, int g, int sk, int k0, int k1, int j) {
-    const int row_lim = sk - a.kq + qi;  // last visible key of this row
+    // The new tokens' keys are the last kq of the sequence, from nk0 on.  Row
+    // qi sees every earlier key and new key nk0 + t iff bit t of its mask is
+    // set: the tokens before it for a chain (causal), its ancestors and
+    // itself in a draft tree.
+    const int nk0 = sk - a.kq;
+    uint32_t vis_new;
+    if (a.tree_mask != nullptr)
+      vis_new = row_ok ? a.tree_mask[(size_t)b * a.kq + qi] : 0u;
+    else
+      vis_new = (2u << qi) - 1u;  // qi < 32; 2u << 31 wraps to 0 and gives all ones
     const uint16_t* Kb = a.k + (size_t)(b * a.Hkv + g) * a.cache_stride * D;
     const uint16_t* Vb = a.v + (size_t)(b * a.Hkv + g) * a.cache_stride * D;
 
@@ -258,12 +268,20 @@ __global__ void __launch_bounds__(kThreads, 1) verify_split_kernel(SplitArgs a) 
         const u32x4 kf = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(kt + k_off[ks]);
         s = mfma_32x32x16_bf16(kf, qf[ks], s);
       }
-      // causal among the new tokens, end of the piece
-      if (key0 + kStep - 1 > sk - a.kq || key0 + kStep > k1) {
-        const int lim = min(row_lim, k1 - 1) - key0 - 4 * h;
+      // mask among the new tokens, end of the piece: bit i of vis is set
+      // iff key key0 + i is visible to this lane's row (every key before
+      // nk0, new key nk0 + t iff bit t of vis_new, nothing from k1 on);
+      // register r holds key 4h + 8(r/4) + r%4 of the step
+      if (key0 + kStep - 1 >= nk0 || key0 + kStep > k1) {
+        const int dn = nk0 - key0;  // step position of new key 0
+        const int dk = k1 - key0;   // step positions [0, dk) are inside the piece
+        const uint32_t old_keys = dn <= 0 ? 0u : (dn >= 32 ? 0xffffffffu : (1u << dn) - 1u);
+        const uint64_t shifted = dn >= 0 ? ((uint64_t)vis_new << min(dn, 32)) : ((uint64_t)vis_new >> min(-dn, 32));
+        const uint32_t in_piece = dk <= 0 ? 0u : (dk >= 32 ? 0xffffffffu : (1u << dk) - 1u);
+        const uint32_t vis = ((old_keys | (uint32_t)shifted) & in_piece) >> (4 * h);
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (8 * (r / 4) + (r % 4) > lim) s[r] = -INFINITY;
+          s[r] = ((vis >> (8 * (r / 4) + (r % 4))) & 1u) ? s[r] : -INFINITY;
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -549,6 +567,7 @@ hipError_t launch(const VerifyArgs& p, hipStream_t s) {
   sa.max_blocks = p.max_blocks;
   sa.num_pages = p.num_pages;
   sa.page_shift = p.page_shift;
+  sa.tree_mask = p.tree_mask;
   sa.part_o = part_o;
   sa.part_lse = part_lse;
   sa.seg_np = seg_np;

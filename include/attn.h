@@ -118,6 +118,30 @@ int attn_verify(const void* q, const void* k_cache, const void* v_cache,
                 void* stream);
 
 /*
+ * attn_verify_tree -- attn_verify for a draft *tree* instead of a chain
+ * ("Making Decode Fast", §3: proposing a tree of candidates and verifying it
+ * with tree attention in one pass raises the acceptance length).  The kq new
+ * tokens of sequence b are tree nodes whose keys are the last kq of its
+ * seqlens_k[b] keys (node t at position seqlens_k[b] - kq + t).  Node i sees
+ * every earlier cache key and new key t iff bit t of tree_mask[b][i] is set
+ * (normally its ancestors and itself).  The causal chain is
+ * tree_mask[b][i] = 2^(i+1) - 1, for which the result equals attn_verify's
+ * bit for bit.  A row that sees no key gets O = 0, lse = -inf.
+ *
+ *   tree_mask   [B, kq] uint32 (device); kq <= 32 follows from the packing
+ *               limit (H / Hkv) * kq <= 32
+ *
+ * All other arguments, the workspace and the errors are those of
+ * attn_verify, plus ATTN_ERR_INVALID_ARG for a null or misaligned tree_mask
+ * when B > 0.
+ */
+int attn_verify_tree(const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* seqlens_k, int max_seqlen_k, int cache_stride,
+                     const uint32_t* tree_mask, void* o, float* lse, int B, int H, int Hkv,
+                     int kq, int d, float scale, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
  * attn_verify_paged -- attn_verify on a paged KV cache ("Warmup Guide --
  * Inference Optimization at Depth", Ch.8: the cache is stored in fixed-size
  * blocks of tokens and each sequence owns a block table mapping its logical

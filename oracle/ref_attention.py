@@ -215,6 +215,61 @@ def verify(q, k_cache, v_cache, seqlens_k, scale: float,
     return out, lse
 
 
+def _masked_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, vis: np.ndarray, scale: float):
+    """O [R, dv] and LSE [R] for one head with an explicit visibility matrix
+    vis [R, Sk]: S = scale * q k^T materialised, -inf where not visible, then
+    the three sweeps of "Warmup Guide", Ch.2 (max, sum of exponentials,
+    normalised probabilities), O = P v and LSE = m + ln l.  Rows that see
+    nothing: O = 0, LSE = -inf."""
+    R = q.shape[0]
+    s = scale * (q @ k.T)
+    s = np.where(vis, s, -np.inf)
+    o = np.zeros((R, v.shape[1]), dtype=np.float64)
+    lse = np.full(R, -np.inf, dtype=np.float64)
+    for i in range(R):
+        if not vis[i].any():
+            continue
+        m = np.max(s[i])
+        e = np.exp(s[i] - m)
+        l_ = np.sum(e)
+        o[i] = (e / l_) @ v
+        lse[i] = m + math.log(l_)
+    return o, lse
+
+
+def verify_tree(q, k_cache, v_cache, seqlens_k, tree_mask, scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Tree-attention verify: the kq new tokens of a sequence are the nodes of
+    a draft tree scored in one verify pass ("Making Decode Fast", §3, trees
+    beat chains: candidates proposed as a tree and verified with tree
+    attention).  Node t's key is at position seqlens_k[b] - kq + t; node i
+    sees every earlier cache key and new key t iff bit t of tree_mask[b][i]
+    is set (its ancestors and itself for a tree; 2^(i+1) - 1 for the causal
+    chain of ``verify``).  q: [B, H, kq, d]; caches [B, Hkv, Smax, d];
+    tree_mask [B, kq] of non-negative ints.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, H, kq, d = q.shape
+    Hkv = np.asarray(k_cache).shape[1]
+    G = H // Hkv
+    sl = [int(x) for x in np.asarray(seqlens_k).reshape(-1)]
+    masks = np.asarray(tree_mask).astype(np.int64) & 0xFFFFFFFF
+    out = np.zeros((B, H, kq, np.asarray(v_cache).shape[3]), dtype=np.float64)
+    lse = np.full((B, H, kq), -np.inf, dtype=np.float64)
+    for b in range(B):
+        n = sl[b]
+        nk0 = n - kq  # position of new token 0
+        vis = np.zeros((kq, n), dtype=bool)
+        for i in range(kq):
+            for t in range(n):
+                rel = t - nk0
+                vis[i, t] = rel < 0 or bool((int(masks[b, i]) >> rel) & 1)
+        k_b = np.asarray(k_cache[b, :, :n], dtype=np.float64)
+        v_b = np.asarray(v_cache[b, :, :n], dtype=np.float64)
+        for h in range(H):
+            out[b, h], lse[b, h] = _masked_head(q[b, h], k_b[h // G], v_b[h // G], vis, scale)
+    return out, lse
+
+
 def gather_paged(pages, block_table, seqlens_k, page_size: int) -> np.ndarray:
     """The logical cache [B, Hkv, max_len, d] held by a paged store.
 

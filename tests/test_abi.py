@@ -180,3 +180,16 @@ def test_verify_paged_rejects(kw, code):
 def test_verify_paged_empty_batch_is_a_noop():
     assert call_paged(B=0, q=None, o=None, sl=None, table=None, k=None, v=None, ws=None, maxs=0,
                       npages=0) == bd.ATTN_OK
+
+
+def test_verify_tree_rejects_missing_mask():
+    a = verify_args()
+    args = (a["q"], a["k"], a["v"], a["sl"], a["maxs"], a["stride"])
+    tail = (a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["kq"], a["d"], a["scale"], a["dtype"], a["ws"], a["wsb"],
+            a["stream"])
+    assert bd.attn_verify_tree(*args, None, *tail) == bd.ATTN_ERR_INVALID_ARG
+    assert bd.attn_verify_tree(*args, FAKE + 2, *tail) == bd.ATTN_ERR_INVALID_ARG
+    a0 = verify_args(B=0, q=None, o=None, sl=None, k=None, v=None, ws=None, maxs=0, stride=0)
+    assert bd.attn_verify_tree(a0["q"], a0["k"], a0["v"], a0["sl"], 0, 0, None, a0["o"], a0["lse"], 0, a0["H"],
+                               a0["Hkv"], a0["kq"], a0["d"], a0["scale"], a0["dtype"], None, a0["wsb"],
+                               None) == bd.ATTN_OK

@@ -492,3 +492,94 @@ def test_verify_paged_equals_contiguous_under_any_page_permutation(page):
     o_p, l_p = ref.verify_paged(q, kp, vp, table, sl, page, 0.4)
     np.testing.assert_array_equal(o_p, o_c)
     np.testing.assert_array_equal(l_p, l_c)
+
+
+# ---------------------------------------------------------------- tree verify
+def chain_masks(B, kq):
+    return np.array([[(1 << (i + 1)) - 1 for i in range(kq)]] * B)
+
+
+def ancestor_masks(parents):
+    """Bitmask of each node's ancestors and itself from a parent array (-1 = root)."""
+    out = []
+    for i in range(len(parents)):
+        m, j = 0, i
+        while j >= 0:
+            m |= 1 << j
+            j = parents[j]
+        out.append(m)
+    return out
+
+
+def test_verify_tree_chain_mask_is_causal_verify():
+    rng = np.random.default_rng(21)
+    B, H, Hkv, kq, d = 3, 4, 2, 5, 8
+    sl = np.array([12, 5, 30])
+    q = rng.standard_normal((B, H, kq, d))
+    k = rng.standard_normal((B, Hkv, 30, d))
+    v = rng.standard_normal((B, Hkv, 30, d))
+    o_c, l_c = ref.verify(q, k, v, sl, 0.35)
+    o_t, l_t = ref.verify_tree(q, k, v, sl, chain_masks(B, kq), 0.35)
+    np.testing.assert_allclose(o_t, o_c, atol=1e-13)
+    np.testing.assert_allclose(l_t, l_c, atol=1e-13)
+
+
+def test_verify_tree_each_root_to_leaf_path_is_a_chain():
+    """A node of a draft tree sees exactly the cache and its root-to-node path,
+    so re-running the path alone as a chain verify must give its row."""
+    rng = np.random.default_rng(22)
+    parents = [-1, 0, 0, 1, 1, 2, 5, 3]
+    kq, H, Hkv, d, L = len(parents), 4, 2, 8, 9
+    q = rng.standard_normal((1, H, kq, d))
+    k = rng.standard_normal((1, Hkv, L + kq, d))
+    v = rng.standard_normal((1, Hkv, L + kq, d))
+    masks = np.array([ancestor_masks(parents)])
+    o_t, l_t = ref.verify_tree(q, k, v, [L + kq], masks, 0.5)
+    leaves = [i for i in range(kq) if i not in parents]
+    assert leaves == [4, 6, 7]
+    for leaf in leaves:
+        path, j = [], leaf
+        while j >= 0:
+            path.append(j)
+            j = parents[j]
+        path = path[::-1]
+        sel = [L + t for t in path]
+        kk = np.concatenate([k[:, :, :L], k[:, :, sel]], axis=2)
+        vv = np.concatenate([v[:, :, :L], v[:, :, sel]], axis=2)
+        o_c, l_c = ref.verify(q[:, :, path], kk, vv, [L + len(path)], 0.5)
+        np.testing.assert_allclose(o_t[:, :, path], o_c, atol=1e-13)
+        np.testing.assert_allclose(l_t[:, :, path], l_c, atol=1e-13)
+
+
+def test_verify_tree_hand_example():
+    """d = 1, scale = 1, q = 1: logits are the keys, chosen as ln w, so the
+    probabilities are w / sum(w) over the visible keys.  Cache key w=2 (v=10);
+    tree root n0 (w=3, v=20) with children n1 (w=5, v=30) and n2 (w=7, v=50).
+    n2 must not see its sibling n1."""
+    w = [2, 3, 5, 7]
+    vals = [10, 20, 30, 50]
+    k = np.log(np.array(w, dtype=np.float64)).reshape(1, 1, 4, 1)
+    v = np.array(vals, dtype=np.float64).reshape(1, 1, 4, 1)
+    q = np.ones((1, 1, 3, 1))
+    masks = np.array([ancestor_masks([-1, 0, 0])])  # [0b001, 0b011, 0b101]
+    o, lse = ref.verify_tree(q, k, v, [4], masks, 1.0)
+    expect = {0: [0, 1], 1: [0, 1, 2], 2: [0, 1, 3]}  # visible key indices
+    for i, vis in expect.items():
+        num = sum(Fraction(w[t]) * vals[t] for t in vis)
+        den = sum(Fraction(w[t]) for t in vis)
+        assert abs(o[0, 0, i, 0] - float(num / den)) < 1e-12
+        assert abs(lse[0, 0, i] - math.log(float(den))) < 1e-12
+    # the chain would have let n2 see n1
+    o_c, _ = ref.verify(q, k, v, [4], 1.0)
+    assert abs(o_c[0, 0, 2, 0] - float(Fraction(580, 17))) < 1e-12
+
+
+def test_verify_tree_empty_rows():
+    """No cache keys and a node whose mask is 0: O = 0, LSE = -inf."""
+    q = np.ones((1, 1, 2, 3))
+    k = np.ones((1, 1, 2, 3))
+    v = np.ones((1, 1, 2, 3))
+    o, lse = ref.verify_tree(q, k, v, [2], np.array([[0, 3]]), 1.0)
+    assert np.all(o[0, 0, 0] == 0) and np.isneginf(lse[0, 0, 0])
+    np.testing.assert_allclose(o[0, 0, 1], 1.0)
+    assert abs(lse[0, 0, 1] - (3.0 + math.log(2.0))) < 1e-12

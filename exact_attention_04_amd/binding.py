@@ -4,8 +4,9 @@ Argument marshalling only: torch tensors supply device memory and the current
 stream, every step of the computation runs in the library's HIP kernels.  The
 raw entry points keep the C names (``attn_fwd``, ``attn_verify``,
 ``attn_verify_tree``, ``attn_verify_paged``, ``attn_verify_workspace_bytes``,
-``attn_strerror``); ``fwd``, ``verify``, ``verify_tree`` and ``verify_paged``
-are tensor-level conveniences over them.  Importing this module raises if the
+``attn_spec_accept``, ``attn_spec_accept_workspace_bytes``,
+``attn_strerror``); ``fwd``, ``verify``, ``verify_tree``, ``verify_paged`` and
+``spec_accept`` are tensor-level conveniences over them.  Importing this module raises if the
 library has not been built: there is no fallback path.
 """
 from __future__ import annotations
@@ -47,11 +48,15 @@ lib.attn_verify_tree.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _i, 
 lib.attn_verify_paged.restype = _i
 lib.attn_verify_paged.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,
                                   _vp, _sz, _vp]
+lib.attn_spec_accept_workspace_bytes.restype = _sz
+lib.attn_spec_accept_workspace_bytes.argtypes = [_i, _i]  # B, V
+lib.attn_spec_accept.restype = _i
+lib.attn_spec_accept.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp]
 lib.attn_strerror.restype = ctypes.c_char_p
 lib.attn_strerror.argtypes = [_i]
 
 EXPORTED = ("attn_fwd", "attn_verify", "attn_verify_tree", "attn_verify_paged", "attn_verify_workspace_bytes",
-            "attn_strerror")
+            "attn_spec_accept", "attn_spec_accept_workspace_bytes", "attn_strerror")
 
 
 class AttnError(RuntimeError):
@@ -94,6 +99,17 @@ def attn_verify_paged(q, k_pages, v_pages, block_table, max_blocks_per_seq, num_
     return lib.attn_verify_paged(q, k_pages, v_pages, block_table, max_blocks_per_seq, num_pages, page_size,
                                  seqlens_k, max_seqlen_k, o, lse, B, H, Hkv, kq, d, float(scale), dtype,
                                  workspace, workspace_bytes, stream)
+
+
+def attn_spec_accept_workspace_bytes(B, V) -> int:
+    return int(lib.attn_spec_accept_workspace_bytes(B, V))
+
+
+def attn_spec_accept(draft_tokens, draft_probs, target_probs, u_accept, u_sample, n_accepted, out_tokens, B, k, V,
+                     workspace, workspace_bytes, stream) -> int:
+    """Raw C entry point (device pointers as ints); returns the ATTN_* code."""
+    return lib.attn_spec_accept(draft_tokens, draft_probs, target_probs, u_accept, u_sample, n_accepted, out_tokens,
+                                B, k, V, workspace, workspace_bytes, stream)
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -219,3 +235,30 @@ def verify_tree(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, s
     if rc != ATTN_OK:
         raise AttnError(rc, "attn_verify_tree")
     return out, lse
+
+
+def spec_accept(draft_tokens: torch.Tensor, draft_probs: torch.Tensor, target_probs: torch.Tensor,
+                u_accept: torch.Tensor, u_sample: torch.Tensor,
+                workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(n_accepted [B], out_tokens [B, k+1]) of the acceptance rule; draft_tokens [B, k] int32,
+    draft_probs [B, k, V] and target_probs [B, k+1, V] fp32, u_accept [B, k] and u_sample [B] fp32."""
+    B, k1, V = target_probs.shape
+    k = k1 - 1
+    for t, dt in ((draft_tokens, torch.int32), (draft_probs, torch.float32), (target_probs, torch.float32),
+                  (u_accept, torch.float32), (u_sample, torch.float32)):
+        if t.dtype != dt:
+            raise TypeError(f"expected {dt}, got {t.dtype}")
+    if tuple(draft_tokens.shape) != (B, k) or tuple(draft_probs.shape) != (B, k, V) or \
+            tuple(u_accept.shape) != (B, k) or tuple(u_sample.shape) != (B,):
+        raise ValueError("inconsistent shapes")
+    dev = target_probs.device
+    n_acc = torch.empty(B, dtype=torch.int32, device=dev)
+    out = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    need = attn_spec_accept_workspace_bytes(B, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    rc = attn_spec_accept(_ptr(draft_tokens), _ptr(draft_probs), _ptr(target_probs), _ptr(u_accept), _ptr(u_sample),
+                          _ptr(n_acc), _ptr(out), B, k, V, _ptr(workspace), workspace.numel(), _stream(target_probs))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_spec_accept")
+    return n_acc, out

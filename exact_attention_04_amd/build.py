@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 
-SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "verify_bf16.hip"]
+SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "verify_bf16.hip", "spec_accept.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU instructions are disabled for all device code.

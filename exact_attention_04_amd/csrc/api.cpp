@@ -190,6 +190,46 @@ extern "C" int attn_verify_paged(const void* q, const void* k_pages, const void*
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+extern "C" size_t attn_spec_accept_workspace_bytes(int B, int V) {
+  if (B < 0 || V < 1 || V > (1 << 22)) return 0;
+  return attn::spec_accept_workspace_bytes(B, V);
+}
+
+extern "C" int attn_spec_accept(const int32_t* draft_tokens, const float* draft_probs,
+                                const float* target_probs, const float* u_accept,
+                                const float* u_sample, int32_t* n_accepted, int32_t* out_tokens,
+                                int B, int k, int V, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (B < 0 || k < 0 || V < 1) return ATTN_ERR_INVALID_ARG;
+  if (V > (1 << 22)) return ATTN_ERR_UNSUPPORTED;  // fixed-point sums stay below 2^62
+  if ((size_t)B * (k + 1) * V > kMaxElems) return ATTN_ERR_INVALID_ARG;
+  if (B == 0) return ATTN_OK;
+  const size_t nq = (size_t)B * k * V;
+  if (k > 0 && (draft_tokens == nullptr || !aligned4(draft_tokens) || u_accept == nullptr ||
+                !aligned4(u_accept) || nq == 0 || draft_probs == nullptr || !aligned4(draft_probs)))
+    return ATTN_ERR_INVALID_ARG;
+  if (target_probs == nullptr || !aligned4(target_probs) || u_sample == nullptr || !aligned4(u_sample) ||
+      n_accepted == nullptr || !aligned4(n_accepted) || out_tokens == nullptr || !aligned4(out_tokens))
+    return ATTN_ERR_INVALID_ARG;
+  const size_t need = attn::spec_accept_workspace_bytes(B, V);
+  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 7u) != 0) return ATTN_ERR_INVALID_ARG;
+  attn::SpecAcceptArgs a;
+  a.draft_tokens = draft_tokens;
+  a.draft_probs = draft_probs;
+  a.target_probs = target_probs;
+  a.u_accept = u_accept;
+  a.u_sample = u_sample;
+  a.n_accepted = n_accepted;
+  a.out_tokens = out_tokens;
+  a.B = B;
+  a.k = k;
+  a.V = V;
+  a.workspace = workspace;
+  const hipError_t e = attn::launch_spec_accept(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 extern "C" const char* attn_strerror(int code) {
   switch (code) {
     case ATTN_OK: return "success";

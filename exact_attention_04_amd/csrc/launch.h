@@ -35,13 +35,27 @@ struct VerifyArgs {
   void* workspace;
 };
 
+struct SpecAcceptArgs {
+  const int32_t* draft_tokens;  // [B][k]
+  const float* draft_probs;     // [B][k][V]
+  const float* target_probs;    // [B][k+1][V]
+  const float* u_accept;        // [B][k]
+  const float* u_sample;        // [B]
+  int32_t* n_accepted;          // [B]
+  int32_t* out_tokens;          // [B][k+1]
+  int B, k, V;
+  void* workspace;
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_verify_bf16(const VerifyArgs& a, hipStream_t s);
+hipError_t launch_spec_accept(const SpecAcceptArgs& a, hipStream_t s);
 
 // Workgroups of the verify split kernel and the workspace it needs.
 int verify_split_workgroups();
 size_t verify_workspace_bytes(int B, int H, int Hkv, int kq, int d);
+size_t spec_accept_workspace_bytes(int B, int V);
 
 }  // namespace attn

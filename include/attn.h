@@ -173,6 +173,58 @@ int attn_verify_paged(const void* q, const void* k_pages, const void* v_pages,
                       float scale, int dtype, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/*
+ * attn_spec_accept_workspace_bytes -- bytes of device workspace
+ * attn_spec_accept needs: two int64 sums per (sequence, 4096-entry chunk of
+ * the vocabulary).  Returns 0 for invalid sizes.
+ */
+size_t attn_spec_accept_workspace_bytes(int B, int V);
+
+/*
+ * attn_spec_accept -- the acceptance rule of speculative decoding, applied to
+ * B sequences after one verify pass ("Warmup Guide -- Inference Optimization
+ * at Depth", Ch.6: accept drafted token x with probability min(1, p(x)/q(x));
+ * at the first rejection resample from norm(max(0, p - q)) and discard the
+ * rest of the draft; "FlashAttention, speculative decoding, quantisation and
+ * parallelism", Mechanics / Speculative decoding: if all k drafts survive, one
+ * more token is sampled from the target's distribution at position k).  The
+ * output is then distributed exactly as sampling the target alone.
+ *
+ *   draft_tokens  [B, k]       int32  drafted tokens (device)
+ *   draft_probs   [B, k, V]    fp32   draft distributions q_i (device)
+ *   target_probs  [B, k+1, V]  fp32   target distributions p_i (device)
+ *   u_accept      [B, k]       fp32   uniforms in [0, 1): draft i of
+ *                                     sequence b is accepted iff
+ *                                     u_accept[b][i] < min(1, p_i(x)/q_i(x))
+ *                                     (fp32, correctly rounded division); a
+ *                                     token with q_i(x) = 0 is accepted iff
+ *                                     p_i(x) > 0; a token outside [0, V) is
+ *                                     rejected
+ *   u_sample      [B]          fp32   uniform in [0, 1) that picks the extra
+ *                                     token by inverse CDF
+ *   n_accepted    [B]          int32  written: accepted drafts j (0..k)
+ *   out_tokens    [B, k+1]     int32  written: the j accepted drafts, the
+ *                                     sampled token, then -1
+ *
+ * Sampling: weights w (the residual max(0, p_j - q_j) after a rejection at
+ * j, else p_k), each clamped to [0, 1] (NaN as 0), are put on a fixed-point
+ * grid W = floor(w * 2^40); with T = floor(u_sample * sum W) (clamped to
+ * [0, sum W - 1]) the token is the first index whose running sum of W exceeds
+ * T.  A residual with no mass falls back to p_j; a distribution with no mass
+ * at all gives token -1.  The random numbers are the caller's; the library
+ * draws none.
+ *
+ * Sizes: B, k >= 0; 1 <= V <= 2^22 (ATTN_ERR_UNSUPPORTED above).  Pointers
+ * must be 4-byte aligned (workspace: 8-byte), non-null unless their tensor is
+ * empty.  Errors: ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED,
+ * ATTN_ERR_WORKSPACE, ATTN_ERR_HIP.  Work is enqueued on `stream`.
+ */
+int attn_spec_accept(const int32_t* draft_tokens, const float* draft_probs,
+                     const float* target_probs, const float* u_accept,
+                     const float* u_sample, int32_t* n_accepted, int32_t* out_tokens,
+                     int B, int k, int V, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
 /* Static, human-readable name of an ATTN_* return code. */
 const char* attn_strerror(int code);
 

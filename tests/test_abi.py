@@ -193,3 +193,42 @@ def test_verify_tree_rejects_missing_mask():
     assert bd.attn_verify_tree(a0["q"], a0["k"], a0["v"], a0["sl"], 0, 0, None, a0["o"], a0["lse"], 0, a0["H"],
                                a0["Hkv"], a0["kq"], a0["d"], a0["scale"], a0["dtype"], None, a0["wsb"],
                                None) == bd.ATTN_OK
+
+
+def call_spec(**kw):
+    a = dict(x=FAKE, q=FAKE, p=FAKE, ua=FAKE, us=FAKE, n=FAKE, out=FAKE, B=8, k=5, V=32000, ws=FAKE, wsb=None,
+             stream=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = bd.attn_spec_accept_workspace_bytes(a["B"], a["V"])
+    return bd.attn_spec_accept(a["x"], a["q"], a["p"], a["ua"], a["us"], a["n"], a["out"], a["B"], a["k"], a["V"],
+                               a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(q=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(p=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(ua=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(us=FAKE + 2), bd.ATTN_ERR_INVALID_ARG),
+    (dict(n=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(out=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(ws=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(ws=FAKE + 4), bd.ATTN_ERR_INVALID_ARG),
+    (dict(k=-1), bd.ATTN_ERR_INVALID_ARG),
+    (dict(V=0), bd.ATTN_ERR_INVALID_ARG),
+    (dict(V=(1 << 22) + 1), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(wsb=8), bd.ATTN_ERR_WORKSPACE),
+])
+def test_spec_accept_rejects(kw, code):
+    assert call_spec(**kw) == code
+
+
+def test_spec_accept_workspace_and_noop():
+    assert bd.attn_spec_accept_workspace_bytes(8, 4096) == 8 * 1 * 16
+    assert bd.attn_spec_accept_workspace_bytes(8, 4097) == 8 * 2 * 16
+    assert bd.attn_spec_accept_workspace_bytes(1, 0) == 0
+    assert bd.attn_spec_accept_workspace_bytes(1, (1 << 22) + 1) == 0
+    assert call_spec(B=0, x=None, q=None, p=None, ua=None, us=None, n=None, out=None, ws=None) == bd.ATTN_OK
+    # k = 0 needs no draft arrays
+    assert call_spec(k=0, x=None, q=None, ua=None, wsb=0) == bd.ATTN_ERR_WORKSPACE

@@ -1,0 +1,99 @@
+"""GPU parity of attn_spec_accept (speculative acceptance rule) against the CPU
+reference: the accepted counts and the output tokens must match exactly
+(integer results; the fp32 acceptance test and the fixed-point inverse CDF
+are decided in the same precision on both sides).
+
+Rule: "Warmup Guide -- Inference Optimization at Depth", Ch.6; the extra token
+after a fully accepted draft: "FlashAttention, speculative decoding,
+quantisation and parallelism", Mechanics / Speculative decoding.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import ref_spec as S
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    from exact_attention_04_amd import binding
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return binding
+
+
+def dists(rng, shape, alpha=0.3):
+    x = rng.gamma(alpha, size=shape).astype(np.float32)
+    return (x / x.sum(axis=-1, keepdims=True)).astype(np.float32)
+
+
+def make_case(seed, B, k, V, mix=0.6):
+    """Target and draft distributions that overlap (draft = mix * target +
+    (1 - mix) * noise), drafts drawn from the draft distribution."""
+    rng = np.random.default_rng(seed)
+    p = dists(rng, (B, k + 1, V))
+    noise = dists(rng, (B, k, V))
+    q = (mix * p[:, :k] + (1 - mix) * noise).astype(np.float32)
+    x = np.zeros((B, k), dtype=np.int32)
+    for b in range(B):
+        for i in range(k):
+            c = np.cumsum(q[b, i].astype(np.float64))
+            x[b, i] = min(int(np.searchsorted(c, rng.random() * c[-1], side="right")), V - 1)
+    u_acc = rng.random((B, k), dtype=np.float32)
+    u_smp = rng.random(B, dtype=np.float32)
+    return x, q, p, u_acc, u_smp
+
+
+def run_and_check(x, q, p, u_acc, u_smp, what):
+    from exact_attention_04_amd import binding
+    B, k1, V = p.shape
+    P.log(f"[spec] {what} B={B} k={k1 - 1} V={V}")
+    n_g, out_g = binding.spec_accept(torch.from_numpy(x).cuda(), torch.from_numpy(q).cuda(),
+                                     torch.from_numpy(p).cuda(), torch.from_numpy(u_acc).cuda(),
+                                     torch.from_numpy(u_smp).cuda())
+    torch.cuda.synchronize()
+    n_r, out_r = S.spec_accept(x, q, p, u_acc, u_smp)
+    np.testing.assert_array_equal(n_g.cpu().numpy(), n_r, err_msg=f"{what}: n_accepted")
+    np.testing.assert_array_equal(out_g.cpu().numpy(), out_r, err_msg=f"{what}: tokens")
+    P.log(f"    ok: accepted {n_r.tolist()[:16]}")
+    return n_r
+
+
+@pytest.mark.parametrize("k", [0, 1, 5, 8])
+@pytest.mark.parametrize("V", [7, 4096, 4097, 32000, 131072])
+def test_random_cases(k, V):
+    B = 64 if V <= 32000 else 16
+    run_and_check(*make_case(k * 1000 + V, B, k, V), what="random")
+
+
+def test_large_vocabulary():
+    run_and_check(*make_case(5, 2, 2, 1 << 22), what="V=2^22")
+
+
+def test_edge_cases():
+    """Forced rejections with p = q (residual without mass: fallback to p),
+    a draft outside the vocabulary, q(x) = 0, uniforms 0 and NaN, an
+    all-zero target row (token -1), and full acceptance."""
+    rng = np.random.default_rng(9)
+    B, k, V = 6, 3, 300
+    p = dists(rng, (B, k + 1, V))
+    q = p[:, :k].copy()
+    x = np.argmax(q, axis=-1).astype(np.int32)
+    u_acc = np.full((B, k), 0.5, dtype=np.float32)
+    u_smp = rng.random(B, dtype=np.float32)
+    u_acc[0, 1] = 1.0             # p = q: min(1, p/q) = 1 is not > 1.0 -> reject, no residual mass
+    x[1, 0] = V + 3               # outside the vocabulary
+    q[2, 0, x[2, 0]] = 0.0        # q(x) = 0, p(x) > 0: kept
+    u_smp[3] = 0.0
+    u_smp[4] = np.nan
+    p[5, 3] = 0.0                 # full acceptance, bonus row without mass
+    run_and_check(x, q, p, u_acc, u_smp, what="edges")
+
+
+def test_verify_workload_shape():
+    """Eight sequences (the verify workload's batch), k = 5, a 131072-entry
+    vocabulary."""
+    n = run_and_check(*make_case(4, 8, 5, 131072, mix=0.8), what="verify-batch")
+    assert n.min() >= 0 and n.max() <= 5

@@ -17,6 +17,12 @@ Prints one JSON line: value = prefill TFLOP/s (causal FLOPs halved:
 every valid cache row plus Q, O and LSE, per call) rides along under
 "verify".  The CPU-baseline leg times the fp64 oracle on a bounded sample of
 the prefill workload (whole heads) on the host cores.
+
+After the timed steps, the entry points beyond the step are measured on the
+same verify workload, each against the HBM roofline ("extras"):
+attn_verify_paged (64-key pages in random physical order), attn_verify_tree
+(a random 5-node draft tree per sequence) and attn_spec_accept (8 sequences,
+k = 5, a 131072-entry vocabulary).
 """
 from __future__ import annotations
 
@@ -87,6 +93,134 @@ def cpu_baseline(w, max_seconds_hint: float = 20.0) -> dict:
             "sample": f"all {n_heads} (batch, head) pairs of {w.name}, all {w.Sq} query rows, "
                       f"fp64 materialised rows, {cores} worker threads; {dt:.1f} s wall; "
                       f"causal FLOPs halved like the GPU figure"}
+
+
+def timed_us(fn, n: int, stream) -> np.ndarray:
+    """Per-call durations (us) of fn(i) from HIP events on `stream`."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        ev[i].record(stream)
+        fn(i)
+    ev[n].record(stream)
+    torch.cuda.synchronize()
+    return np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n)])
+
+
+def paged_copy(k, v, seqlens, page, rng):
+    """Pages [num_pages, Hkv, page, d] holding caches [B, Hkv, S, d] in random
+    physical order, and the int32 block table."""
+    import torch
+    B, Hkv, S, d = k.shape
+    nblk = [(int(s) + page - 1) // page for s in seqlens]
+    perm = rng.permutation(sum(nblk))
+    kp = torch.zeros((len(perm), Hkv, page, d), dtype=k.dtype, device=k.device)
+    vp = torch.zeros_like(kp)
+    table = np.full((B, max(nblk)), -1, dtype=np.int32)
+    i = 0
+    for b in range(B):
+        for blk in range(nblk[b]):
+            ph = int(perm[i])
+            i += 1
+            table[b, blk] = ph
+            n = min(page, int(seqlens[b]) - blk * page)
+            kp[ph, :, :n] = k[b, :, blk * page:blk * page + n]
+            vp[ph, :, :n] = v[b, :, blk * page:blk * page + n]
+    return kp, vp, torch.from_numpy(table).to(k.device)
+
+
+def tree_masks(rng, B, kq):
+    rows = []
+    for _ in range(B):
+        parents = [-1] + [int(rng.integers(0, i)) for i in range(1, kq)]
+        row = []
+        for i in range(kq):
+            m, j = 0, i
+            while j >= 0:
+                m |= 1 << j
+                j = parents[j]
+            row.append(m)
+        rows.append(row)
+    return np.array(rows, dtype=np.int32)
+
+
+def spec_inputs(B, k, V, dev, seed=12):
+    import torch
+    rng = np.random.default_rng(seed)
+    g = rng.gamma(0.3, size=(B, k + 1, V)).astype(np.float32)
+    p = g / g.sum(-1, keepdims=True)
+    n = rng.gamma(0.3, size=(B, k, V)).astype(np.float32)
+    q = (0.8 * p[:, :k] + 0.2 * n / n.sum(-1, keepdims=True)).astype(np.float32)
+    x = np.argmax(q, axis=-1).astype(np.int32)
+    ua = rng.random((B, k), dtype=np.float32)
+    us = rng.random(B, dtype=np.float32)
+    return [torch.from_numpy(a).to(dev) for a in (x, q, p, ua, us)]
+
+
+def extras(dev, wv, vq, caches, vsl, seqlens, max_len, stream) -> dict:
+    import torch
+    from exact_attention_04_amd import binding
+    rng = np.random.default_rng(7)
+    vbytes = verify_algorithmic_bytes(wv, seqlens)
+    out = {}
+    # paged verify: two page pools in different random orders, alternated
+    pools = [paged_copy(kc, vc, seqlens, 64, rng) for kc, vc in caches[:2]]
+    ws = torch.empty(binding.attn_verify_workspace_bytes(wv.B, wv.H, wv.Hkv, wv.kq, wv.d), dtype=torch.uint8,
+                     device=dev)
+    o = torch.empty_like(vq)
+    lse = torch.empty((wv.B, wv.H, wv.kq), dtype=torch.float32, device=dev)
+
+    def paged(i):
+        kp, vp, table = pools[i % 2]
+        binding.verify_paged(vq, kp, vp, table, vsl, max_len, scale=wv.scale, out=o, lse=lse, workspace=ws)
+    for i in range(5):
+        paged(i)
+    us = timed_us(paged, 50, stream)
+    pbytes = vbytes + int(sum((int(s) + 63) // 64 for s in seqlens)) * 4
+    out["verify_paged"] = {"page": 64, "us_per_call": round(float(us.mean()), 2),
+                           "roofline": {"bound": "hbm", "achieved": round(pbytes / us.mean() / 1e3, 1),
+                                        "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                        "frac": round(pbytes / us.mean() / 1e3 / PEAK_HBM_GBPS, 4),
+                                        "traffic": None}}
+    del pools
+    # tree verify: a random 5-node tree per sequence
+    tm = torch.from_numpy(tree_masks(rng, wv.B, wv.kq)).to(dev)
+
+    def tree(i):
+        kc, vc = caches[i % len(caches)]
+        binding.verify_tree(vq, kc, vc, vsl, max_len, tm, scale=wv.scale, out=o, lse=lse, workspace=ws)
+    for i in range(5):
+        tree(i)
+    us = timed_us(tree, 50, stream)
+    out["verify_tree"] = {"us_per_call": round(float(us.mean()), 2),
+                          "roofline": {"bound": "hbm", "achieved": round(vbytes / us.mean() / 1e3, 1),
+                                       "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                       "frac": round(vbytes / us.mean() / 1e3 / PEAK_HBM_GBPS, 4),
+                                       "traffic": None}}
+    # acceptance rule: 8 sequences, k = 5, V = 131072; two input copies
+    B, k, V = wv.B, wv.kq, 131072
+    sets = [spec_inputs(B, k, V, dev, seed) for seed in (12, 13)]
+    sws = torch.empty(binding.attn_spec_accept_workspace_bytes(B, V), dtype=torch.uint8, device=dev)
+    n_acc = []
+
+    def spec(i):
+        n, _ = binding.spec_accept(*sets[i % 2], workspace=sws)
+        if len(n_acc) < 2:
+            n_acc.append(n)
+    for i in range(5):
+        spec(i)
+    us = timed_us(spec, 50, stream)
+    # bytes: the sampled row of p (and of q after a rejection) for every
+    # sequence, plus the k looked-up entries; averaged over the two sets
+    acc = [a.cpu().numpy() for a in n_acc]
+    sbytes = float(np.mean([sum(V * 4 * (2 if j < k else 1) + k * 16 for j in a.tolist()) for a in acc]))
+    out["spec_accept"] = {"B": B, "k": k, "V": V, "us_per_call": round(float(us.mean()), 2),
+                          "roofline": {"bound": "hbm", "achieved": round(sbytes / us.mean() / 1e3, 1),
+                                       "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                       "frac": round(sbytes / us.mean() / 1e3 / PEAK_HBM_GBPS, 4),
+                                       "traffic": None}}
+    return out
 
 
 def profile_leg(args, dev) -> int:
@@ -224,6 +358,10 @@ def main() -> int:
         "prefill_ms": round(float(pre_ms.mean()), 4),
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
+    out["extras"] = extras(dev, wv, vq, caches, vsl, seqlens, max_len, stream)
+    for name, e in out["extras"].items():
+        log(f"{name}: {e['us_per_call']:.1f} us -> {e['roofline']['achieved']:.0f} GB/s "
+            f"= {100 * e['roofline']['frac']:.1f}% of HBM")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wp)
     print(json.dumps(out), flush=True)

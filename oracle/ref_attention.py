@@ -215,6 +215,50 @@ def verify(q, k_cache, v_cache, seqlens_k, scale: float,
     return out, lse
 
 
+def attention_backward(q, k, v, dout, causal: bool, scale: float):
+    """Gradients (dQ, dK, dV) of sum(dout * O) for O = attention(q, k, v).
+
+    "Warmup Guide -- Inference Optimization at Depth", Ch.4 (backward pass):
+    P is recomputed from Q and K with the per-row statistics of the forward
+    pass instead of being stored.  Here every quantity is materialised in
+    float64 from the definition of Ch.1 (S = scale Q K^T with the mask, P =
+    softmax(S) per row, O = P V), and the gradients are that definition's
+    derivatives:
+        dV = P^T dO;  dP = dO V^T;  dS = P * (dP - rowsum(P * dP));
+        dQ = scale dS K;  dK = scale dS^T Q.
+    For grouped-query attention dK and dV of a KV head sum over the query
+    heads that read it.  Rows that see no key contribute nothing.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, H, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    G = H // Hkv
+    vis = visible_mask(Sq, Sk, causal)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            g = h // G
+            s = scale * (q[b, h] @ k[b, g].T)
+            s = np.where(vis, s, -np.inf)
+            P = np.zeros_like(s)
+            for i in range(Sq):
+                if vis[i].any():
+                    m = np.max(s[i])
+                    e = np.exp(s[i] - m)
+                    P[i] = e / np.sum(e)
+            dv[b, g] += P.T @ dout[b, h]
+            dP = dout[b, h] @ v[b, g].T
+            dS = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
+            dq[b, h] = scale * (dS @ k[b, g])
+            dk[b, g] += scale * (dS.T @ q[b, h])
+    return dq, dk, dv
+
+
 def _masked_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, vis: np.ndarray, scale: float):
     """O [R, dv] and LSE [R] for one head with an explicit visibility matrix
     vis [R, Sk]: S = scale * q k^T materialised, -inf where not visible, then

@@ -583,3 +583,69 @@ def test_verify_tree_empty_rows():
     assert np.all(o[0, 0, 0] == 0) and np.isneginf(lse[0, 0, 0])
     np.testing.assert_allclose(o[0, 0, 1], 1.0)
     assert abs(lse[0, 0, 1] - (3.0 + math.log(2.0))) < 1e-12
+
+
+# ---------------------------------------------------------------- backward
+def loss_and_grads(q, k, v, do, causal, scale):
+    o, _ = ref.attention(q, k, v, causal, scale)
+    return float(np.sum(o * do)), ref.attention_backward(q, k, v, do, causal, scale)
+
+
+@pytest.mark.parametrize("causal,Sq,Sk,H,Hkv", [(False, 5, 7, 2, 1), (True, 6, 6, 2, 2), (True, 4, 9, 4, 2),
+                                               (True, 7, 3, 1, 1)])
+def test_backward_matches_central_differences(causal, Sq, Sk, H, Hkv):
+    """The gradient of L = sum(dO * O) against central finite differences of
+    the forward oracle, for every element of Q, K and V (fp64, step 1e-6)."""
+    rng = np.random.default_rng(41)
+    d = 3
+    q, k, v = rng.standard_normal((1, H, Sq, d)), rng.standard_normal((1, Hkv, Sk, d)), rng.standard_normal((1, Hkv, Sk, d))
+    do = rng.standard_normal((1, H, Sq, d))
+    _, grads = loss_and_grads(q, k, v, do, causal, 0.7)
+    eps = 1e-6
+    for x, gx in zip((q, k, v), grads):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + eps
+            lp, _ = loss_and_grads(q, k, v, do, causal, 0.7)
+            x[idx] = keep - eps
+            lm, _ = loss_and_grads(q, k, v, do, causal, 0.7)
+            x[idx] = keep
+            num[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(gx, num, atol=1e-7, rtol=1e-6)
+
+
+@pytest.mark.parametrize("causal,Sq,Sk", [(False, 33, 20), (True, 40, 40), (True, 17, 50)])
+def test_backward_matches_torch_autograd(causal, Sq, Sk):
+    """torch CPU autograd in fp64 through scaled_dot_product_attention with an
+    explicit bottom-right mask (grouped heads expanded by repeat)."""
+    rng = np.random.default_rng(42)
+    B, H, Hkv, d, scale = 2, 4, 2, 16, 0.3
+    q, k, v = rng.standard_normal((B, H, Sq, d)), rng.standard_normal((B, Hkv, Sk, d)), rng.standard_normal((B, Hkv, Sk, d))
+    do = rng.standard_normal((B, H, Sq, d))
+    dq, dk, dv = ref.attention_backward(q, k, v, do, causal, scale)
+    tq = torch.tensor(q, requires_grad=True)
+    tk = torch.tensor(k, requires_grad=True)
+    tv = torch.tensor(v, requires_grad=True)
+    mask = torch.tensor(ref.visible_mask(Sq, Sk, causal))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk.repeat_interleave(H // Hkv, dim=1), tv.repeat_interleave(H // Hkv, dim=1), attn_mask=mask, scale=scale)
+    (o * torch.tensor(do)).sum().backward()
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-10)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-10)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-10)
+
+
+def test_backward_closed_forms():
+    """One key: P = 1, so dV_0 = sum_i dO_i and dQ = dK = 0.  Rows of dS sum
+    to zero, so the keys' dK vectors sum to zero."""
+    rng = np.random.default_rng(43)
+    q, k, v, do = rng.standard_normal((1, 2, 6, 4)), rng.standard_normal((1, 1, 1, 4)), \
+        rng.standard_normal((1, 1, 1, 4)), rng.standard_normal((1, 2, 6, 4))
+    dq, dk, dv = ref.attention_backward(q, k, v, do, False, 0.5)
+    np.testing.assert_allclose(dv[0, 0, 0], do[0].sum(axis=(0, 1)), atol=1e-12)
+    assert np.abs(dq).max() < 1e-12 and np.abs(dk).max() < 1e-12
+    q, k, v, do = (rng.standard_normal((1, 2, 9, 4)) for _ in range(4))
+    for causal in (False, True):
+        _, dk, _ = ref.attention_backward(q, k, v, do, causal, 0.5)
+        np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)

@@ -4,9 +4,10 @@ Argument marshalling only: torch tensors supply device memory and the current
 stream, every step of the computation runs in the library's HIP kernels.  The
 raw entry points keep the C names (``attn_fwd``, ``attn_verify``,
 ``attn_verify_tree``, ``attn_verify_paged``, ``attn_verify_workspace_bytes``,
-``attn_spec_accept``, ``attn_spec_accept_workspace_bytes``,
-``attn_strerror``); ``fwd``, ``verify``, ``verify_tree``, ``verify_paged`` and
-``spec_accept`` are tensor-level conveniences over them.  Importing this module raises if the
+``attn_spec_accept``, ``attn_spec_accept_workspace_bytes``, ``attn_bwd``,
+``attn_bwd_workspace_bytes``, ``attn_strerror``); ``fwd``, ``bwd``,
+``verify``, ``verify_tree``, ``verify_paged`` and ``spec_accept`` are
+tensor-level conveniences over them.  Importing this module raises if the
 library has not been built: there is no fallback path.
 """
 from __future__ import annotations
@@ -52,11 +53,16 @@ lib.attn_spec_accept_workspace_bytes.restype = _sz
 lib.attn_spec_accept_workspace_bytes.argtypes = [_i, _i]  # B, V
 lib.attn_spec_accept.restype = _i
 lib.attn_spec_accept.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp]
+lib.attn_bwd_workspace_bytes.restype = _sz
+lib.attn_bwd_workspace_bytes.argtypes = [_i, _i, _i]  # B, H, Sq
+lib.attn_bwd.restype = _i
+lib.attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]
 lib.attn_strerror.restype = ctypes.c_char_p
 lib.attn_strerror.argtypes = [_i]
 
 EXPORTED = ("attn_fwd", "attn_verify", "attn_verify_tree", "attn_verify_paged", "attn_verify_workspace_bytes",
-            "attn_spec_accept", "attn_spec_accept_workspace_bytes", "attn_strerror")
+            "attn_spec_accept", "attn_spec_accept_workspace_bytes", "attn_bwd", "attn_bwd_workspace_bytes",
+            "attn_strerror")
 
 
 class AttnError(RuntimeError):
@@ -110,6 +116,17 @@ def attn_spec_accept(draft_tokens, draft_probs, target_probs, u_accept, u_sample
     """Raw C entry point (device pointers as ints); returns the ATTN_* code."""
     return lib.attn_spec_accept(draft_tokens, draft_probs, target_probs, u_accept, u_sample, n_accepted, out_tokens,
                                 B, k, V, workspace, workspace_bytes, stream)
+
+
+def attn_bwd_workspace_bytes(B, H, Sq) -> int:
+    return int(lib.attn_bwd_workspace_bytes(B, H, Sq))
+
+
+def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, Sq, Sk, d, causal, scale, dtype, workspace,
+             workspace_bytes, stream) -> int:
+    """Raw C entry point (device pointers as ints); returns the ATTN_* code."""
+    return lib.attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, Sq, Sk, d, int(causal), float(scale), dtype,
+                        workspace, workspace_bytes, stream)
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -262,3 +279,24 @@ def spec_accept(draft_tokens: torch.Tensor, draft_probs: torch.Tensor, target_pr
     if rc != ATTN_OK:
         raise AttnError(rc, "attn_spec_accept")
     return n_acc, out
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+        dout: torch.Tensor, causal: bool = False, scale: Optional[float] = None,
+        workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """(dQ, dK, dV) for the forward outputs o, lse of fwd(q, k, v) and the upstream gradient dout."""
+    B, H, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    need = attn_bwd_workspace_bytes(B, H, Sq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    rc = attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                  B, H, Hkv, Sq, Sk, d, causal, scale, _dtype_code(q), _ptr(workspace), workspace.numel(), _stream(q))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_bwd")
+    return dq, dk, dv

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 
-SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "verify_bf16.hip", "spec_accept.hip"]
+SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "verify_bf16.hip", "spec_accept.hip", "bwd_bf16.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU instructions are disabled for all device code.
@@ -31,6 +31,14 @@ HIP_FLAGS = [
 ]
 
 
+# Per-source device-compiler options.  The backward kernels run one wave per
+# SIMD with a 512-register budget, where the default would select every MFMA
+# in the AGPR form; the VGPR form lets the vector unit read S and dP directly.
+FILE_FLAGS = {
+    "bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def hipcc() -> str:
     p = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(p):
@@ -40,7 +48,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIP_FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-x")
         cmd.insert(2, "hip")

@@ -230,6 +230,53 @@ extern "C" int attn_spec_accept(const int32_t* draft_tokens, const float* draft_
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+extern "C" size_t attn_bwd_workspace_bytes(int B, int H, int Sq) {
+  if (B < 0 || H < 1 || Sq < 0) return 0;
+  return attn::bwd_workspace_bytes(B, H, Sq);
+}
+
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, int Sq,
+                        int Sk, int d, int causal, float scale, int dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (B < 0 || Sq < 0 || Sk < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || d < 1) return ATTN_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  const size_t nq = (size_t)B * H * Sq * d;
+  const size_t nk = (size_t)B * Hkv * Sk * d;
+  if (nq > kMaxElems || nk > kMaxElems) return ATTN_ERR_INVALID_ARG;
+  if ((size_t)B * H * (size_t)((Sq + 127) / 128) > 0x7fffffffu) return ATTN_ERR_INVALID_ARG;
+  if (!ptr_ok(q, nq) || !ptr_ok(o, nq) || !ptr_ok(dout, nq) || !ptr_ok(dq, nq)) return ATTN_ERR_INVALID_ARG;
+  if (!ptr_ok(k, nk) || !ptr_ok(v, nk) || !ptr_ok(dk, nk) || !ptr_ok(dv, nk)) return ATTN_ERR_INVALID_ARG;
+  if (nq > 0 && (lse == nullptr || !aligned4(lse))) return ATTN_ERR_INVALID_ARG;
+  const size_t need = attn::bwd_workspace_bytes(B, H, Sq);
+  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (need > 0 && (workspace == nullptr || !aligned16(workspace))) return ATTN_ERR_INVALID_ARG;
+  if (nq == 0 && nk == 0) return ATTN_OK;
+  attn::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.B = B;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.Sq = Sq;
+  a.Sk = Sk;
+  a.d = d;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.workspace = workspace;
+  const hipError_t e = attn::launch_bwd_bf16(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 extern "C" const char* attn_strerror(int code) {
   switch (code) {
     case ATTN_OK: return "success";

@@ -1,0 +1,555 @@
+// Backward pass of exact attention (bf16 inputs, fp32 accumulation, gfx950).
+//
+// "Warmup Guide -- Inference Optimization at Depth", Ch.4 (backward pass): P
+// is not stored; it is recomputed tile by tile from Q and K with the per-row
+// statistics kept by the forward pass (here LSE = m + ln l, so P_ij =
+// exp(s_ij - LSE_i)).  The gradients are those of the definition of Ch.1
+// (S = scale Q K^T with the causal mask, P = softmax(S), O = P V):
+//     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),  D_i = sum_j P_ij dP_ij
+//     dQ = scale dS K,   dK = scale dS^T Q,
+// with D_i = rowsum(dO_i * O_i), which equals sum_j P_ij dP_ij because O = P V.
+//
+// Three kernels, no atomics (deterministic):
+//   * bwd_pre: D_i and LSE_i * log2(e) per query row into the workspace;
+//   * bwd_dq: one workgroup per (batch, head, 128 query rows), like the
+//     forward kernel: each wave holds 32 query rows' Q and dO as MFMA B
+//     operands, K/V tiles of 64 keys stream through LDS, and per tile
+//       S^T = K Q^T, dP^T = V dO^T            (scores transposed: lane = query)
+//       dS^T = P^T * (dP^T - D)               (P^T = exp2(S^T c - LSE2))
+//       dQ^T += K^T dS^T                      (K^T by LDS transpose reads);
+//   * bwd_dkdv: one workgroup per (batch, KV head, 128 keys), each wave 32
+//     keys whose K and V rows it holds as MFMA B operands; it walks the query
+//     tiles of every query head that reads its KV head (grouped-query heads
+//     are summed here), Q/dO tiles and their D, LSE2 rows streaming through
+//     LDS, and per 32-row block
+//       S = Q K^T, dP = dO V^T                (lane = key)
+//       dS = P * (dP - D)
+//       dV^T += dO^T P, dK^T += Q^T dS        (dO^T, Q^T by LDS transpose reads).
+//     All MFMAs are compiler builtins selected in the VGPR form (the vector
+//     unit reads S and dP directly); the compiler parks part of the dK/dV
+//     accumulators in AGPRs and tracks every matrix-core wait state itself.
+#include "device_common.h"
+#include "launch.h"
+
+namespace attn {
+namespace {
+
+constexpr int kThreads = 256;  // four waves
+constexpr int kWaves = 4;
+
+struct BwdKArgs {
+  const uint16_t* q;     // [B][H][Sq][D]
+  const uint16_t* k;     // [B][Hkv][Sk][D]
+  const uint16_t* v;
+  const uint16_t* o;     // [B][H][Sq][D]
+  const uint16_t* dout;  // [B][H][Sq][D]
+  const float* lse;      // [B][H][Sq] natural log
+  float* lse2;           // workspace [B][H][Sq]: LSE * log2(e)
+  float* dsum;           // workspace [B][H][Sq]: D
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int B, H, Hkv, Sq, Sk;
+  int nqb;   // 128-row query blocks per (batch, head)
+  int nkb;   // 128-key blocks per (batch, KV head)
+  float c2;  // scale * log2(e)
+  float scale;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t x) { return __builtin_bit_cast(float, x << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t x) { return __builtin_bit_cast(float, x & 0xffff0000u); }
+
+// ---- D = rowsum(dO * O) and the base-2 LSE, D/8 lanes per row
+template <int D>
+__global__ void __launch_bounds__(kThreads) bwd_pre(BwdKArgs a) {
+  constexpr int LPR = D / 8;
+  const long long rows = (long long)a.B * a.H * a.Sq;
+  const long long row = (long long)blockIdx.x * (kThreads / LPR) + threadIdx.x / LPR;
+  const int sub = threadIdx.x % LPR;
+  const bool ok = row < rows;
+  float acc = 0.f;
+  if (ok) {
+    const u32x4 ov = load16(a.o + row * D + sub * 8);
+    const u32x4 dv = load16(a.dout + row * D + sub * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = fmaf(bf16_lo(ov[i]), bf16_lo(dv[i]), acc);
+      acc = fmaf(bf16_hi(ov[i]), bf16_hi(dv[i]), acc);
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (ok && sub == 0) {
+    a.dsum[row] = acc;
+    a.lse2[row] = a.lse[row] * kLog2e;  // -inf stays -inf
+  }
+}
+
+// ---- dQ
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_dq(BwdKArgs a) {
+  constexpr int CPR = D / 8, KS = D / 16, NDB = D / 32;
+  constexpr int BC = 64;  // keys per tile
+  constexpr int TILE = BC * D;
+  constexpr int ROWS_PER_INSN = 1024 / (D * 2);
+  constexpr int IPW = TILE * 2 / 1024 / kWaves;
+  static_assert(IPW >= 1, "every wave loads part of each tile");
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[TILE];
+  typedef const __attribute__((address_space(3))) char lds_cchar;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, h = lane >> 5;
+  const int blk = xcd_grouped_block(blockIdx.x, gridDim.x);
+  const int bh = blk / a.nqb;
+  int qblk = blk - bh * a.nqb;
+  if (CAUSAL) qblk = a.nqb - 1 - qblk;
+  const int b = bh / a.H, hq = bh - b * a.H, g = hq / (a.H / a.Hkv);
+  const int q0 = qblk * 128, wq0 = q0 + 32 * wave, shift = a.Sk - a.Sq;
+  const int row = wq0 + n;
+  const bool row_ok = row < a.Sq;
+  const size_t rbase = (size_t)(b * a.H + hq) * a.Sq;
+  const uint16_t* Q = a.q + rbase * D;
+  const uint16_t* dO = a.dout + rbase * D;
+  const uint16_t* K = uniform_ptr(a.k + (size_t)(b * a.Hkv + g) * a.Sk * D);
+  const uint16_t* V = uniform_ptr(a.v + (size_t)(b * a.Hkv + g) * a.Sk * D);
+
+  int kend = a.Sk;
+  if (CAUSAL) kend = min(a.Sk, min(q0 + 128, a.Sq) + shift);
+  kend = max(kend, 0);
+  const int nkt = (kend + BC - 1) / BC;
+  int nfull = a.Sk / BC;  // tiles [0, nfull) need no mask for this wave's rows
+  if (CAUSAL) nfull = min(nfull, max(wq0 + shift + 1, 0) / BC);
+
+  // per-lane row statistics; rows that see nothing get no gradient
+  const float lse2 = row_ok ? a.lse2[rbase + row] : -INFINITY;
+  const float dsum = row_ok ? a.dsum[rbase + row] : 0.f;
+  const bool live = lse2 != -INFINITY;
+  const float lse_use = live ? lse2 : 0.f;
+
+  u32x4 qf[KS], df[KS];  // Q^T and dO^T B operands (column = this lane's row)
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qf[ks] = row_ok ? load16(Q + (size_t)row * D + ks * 16 + h * 8) : u32x4{0, 0, 0, 0};
+    df[ks] = row_ok ? load16(dO + (size_t)row * D + ks * 16 + h * 8) : u32x4{0, 0, 0, 0};
+  }
+
+  // HBM -> LDS loads (both tiles in the K layout: swizzle chunk ^ (row & 15))
+  uint32_t voff[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int r = (wave * IPW + i) * ROWS_PER_INSN + lane / CPR;
+    voff[i] = (r * D + (((lane % CPR) ^ k_swz<D>(r)) * 8)) * 2;
+  }
+  auto issue = [&](int t, const int BUF) __attribute__((always_inline)) {
+    const int j0 = t * BC;
+    const int bytes = max(a.Sk - j0, 0) * D * 2;
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(K + (size_t)j0 * D), (short)0, bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(V + (size_t)j0 * D), (short)0, bytes, kBufferWord3);
+    uint16_t* kd = BUF ? k_lds1 : k_lds0;
+    uint16_t* vd = BUF ? v_lds1 : v_lds0;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      buffer_load_lds16(kr, kd + (wave * IPW + i) * 512, voff[i]);
+      buffer_load_lds16(vr, vd + (wave * IPW + i) * 512, voff[i]);
+    }
+  };
+
+  // operand offsets: row-major A reads (row n of a 32-key block) and K^T
+  // transpose reads (rows 16t + 4h + r4 and 16t + 8 + 4h + r4, d columns
+  // 32db + 16(gq&1) + 4c4 .. +3)
+  const int gq = lane >> 4, r4 = (lane >> 2) & 3, c4 = lane & 3;
+  uint32_t a_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) a_off[ks] = (n * D + (((ks * 2 + h) ^ k_swz<D>(n)) * 8)) * 2;
+  uint32_t tr_lo[NDB], tr_hi[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int dcol = 32 * db + 16 * (gq & 1) + 4 * c4;
+    const int rl = 4 * h + r4, rh = 8 + 4 * h + r4;
+    tr_lo[db] = (rl * D + (((dcol >> 3) ^ k_swz<D>(rl)) * 8) + (dcol & 7)) * 2;
+    tr_hi[db] = (rh * D + (((dcol >> 3) ^ k_swz<D>(rh)) * 8) + (dcol & 7)) * 2;
+  }
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+
+  auto tile = [&](int j, const int BUF, const bool MASKED) __attribute__((always_inline)) {
+    lds_cchar* kb_ = (lds_cchar*)(BUF ? k_lds1 : k_lds0);
+    lds_cchar* vb_ = (lds_cchar*)(BUF ? v_lds1 : v_lds0);
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 kf = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(kb_ + a_off[ks] + kb * 32 * D * 2);
+        const u32x4 vf = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(vb_ + a_off[ks] + kb * 32 * D * 2);
+        s[kb] = mfma_32x32x16_bf16(kf, qf[ks], s[kb]);
+        dp[kb] = mfma_32x32x16_bf16(vf, df[ks], dp[kb]);
+      }
+    }
+    // register r of block kb: key j0 + 32kb + 8(r/4) + 4h + r%4
+    const int j0 = j * BC;
+    const int lim = (CAUSAL ? min(a.Sk - 1, row + shift) : a.Sk - 1) - j0 - 4 * h;
+    u32x4 dst[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int kb = t >> 1, base = (t & 1) * 8;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float ds2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = base + 2 * w + e;
+          float p = live ? fast_exp2(fmaf(s[kb][r], a.c2, -lse_use)) : 0.f;
+          if (MASKED && kb * 32 + 8 * (r / 4) + (r % 4) > lim) p = 0.f;
+          ds2[e] = p * (dp[kb][r] - dsum);
+        }
+        dst[t][w] = pack_bf16x2(ds2[0], ds2[1]);
+      }
+    }
+    // dQ^T += K^T dS^T over the tile's 16-key steps
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kb_ + tr_lo[db] + 16 * t * D * 2));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kb_ + tr_hi[db] + 16 * t * D * 2));
+        u32x4 af;
+        af[0] = __builtin_bit_cast(u32x2, lo)[0];
+        af[1] = __builtin_bit_cast(u32x2, lo)[1];
+        af[2] = __builtin_bit_cast(u32x2, hi)[0];
+        af[3] = __builtin_bit_cast(u32x2, hi)[1];
+        acc[db] = mfma_32x32x16_bf16(af, dst[t], acc[db]);
+      }
+    }
+  };
+
+  if (nkt > 0) {
+    issue(0, 0);
+    for (int j = 0; j < nkt; j += 2) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int jj = j + u;
+        if (jj < nkt) {
+          if (jj + 1 < nkt) {
+            issue(jj + 1, u ^ 1);
+            wait_vmem_at_most<2 * IPW>();
+          } else {
+            wait_vmem_all();
+          }
+          __syncthreads();  // tile jj is in LDS for every wave
+          if (jj < nfull)
+            tile(jj, u, false);
+          else
+            tile(jj, u, true);
+          __syncthreads();  // everyone is done with buffer u before it is refilled
+        }
+      }
+    }
+  }
+
+  if (row_ok) {
+    uint16_t* out = a.dq + (rbase + row) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const uint32_t w0 = pack_bf16x2(acc[db][4 * rg + 0] * a.scale, acc[db][4 * rg + 1] * a.scale);
+        const uint32_t w1 = pack_bf16x2(acc[db][4 * rg + 2] * a.scale, acc[db][4 * rg + 3] * a.scale);
+        *reinterpret_cast<u32x2*>(out + 32 * db + 8 * rg + 4 * h) = u32x2{w0, w1};
+      }
+  }
+}
+
+// ---- dK, dV
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+bwd_dkdv(BwdKArgs a) {
+  constexpr int CPR = D / 8, KS = D / 16, NDB = D / 32;
+  constexpr int BR = 64;  // query rows per tile
+  constexpr int TILE = BR * D;
+  constexpr int ROWS_PER_INSN = 1024 / (D * 2);
+  constexpr int IPW = TILE * 2 / 1024 / kWaves;
+  static_assert(IPW >= 1, "every wave loads part of each tile");
+  __shared__ __attribute__((aligned(1024))) uint16_t q_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t q_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t d_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t d_lds1[TILE];
+  __shared__ __attribute__((aligned(256))) float st_lds0[2][BR];  // LSE2, D of the tile's rows
+  __shared__ __attribute__((aligned(256))) float st_lds1[2][BR];
+  typedef const __attribute__((address_space(3))) char lds_cchar;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, h = lane >> 5;
+  const int blk = xcd_grouped_block(blockIdx.x, gridDim.x);
+  const int bg = blk / a.nkb;
+  const int kblk = blk - bg * a.nkb;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int G = a.H / a.Hkv;
+  const int k0 = kblk * 128, wk0 = k0 + 32 * wave, shift = a.Sk - a.Sq;
+  const int key = wk0 + n;  // this lane's key
+  const bool key_ok = key < a.Sk;
+  const uint16_t* Kg = a.k + (size_t)(b * a.Hkv + g) * a.Sk * D;
+  const uint16_t* Vg = a.v + (size_t)(b * a.Hkv + g) * a.Sk * D;
+
+  // K^T and V^T B operands of this lane's key
+  u32x4 kf[KS], vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kf[ks] = key_ok ? load16(Kg + (size_t)key * D + ks * 16 + h * 8) : u32x4{0, 0, 0, 0};
+    vf[ks] = key_ok ? load16(Vg + (size_t)key * D + ks * 16 + h * 8) : u32x4{0, 0, 0, 0};
+  }
+
+  // query tiles that see any of the workgroup's keys: rows i with
+  // i + shift >= k0, i.e. from k0 - shift on (causal); all rows otherwise
+  const int qstart = CAUSAL ? max(k0 - shift, 0) : 0;
+  const int t_first = min(qstart, a.Sq) / BR;
+  const int ntq = (a.Sq + BR - 1) / BR - t_first;  // tiles per query head
+  const int ntot = a.Sk > k0 ? ntq * G : 0;
+  // tiles that need no mask for this wave's keys: every row sees every key
+  // of the wave (row >= wk0 + 31 - shift) and rows and keys are in range
+  const int row_full = CAUSAL ? wk0 + 31 - shift : 0;
+
+  uint32_t voff[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int r = (wave * IPW + i) * ROWS_PER_INSN + lane / CPR;
+    voff[i] = (r * D + (((lane % CPR) ^ k_swz<D>(r)) * 8)) * 2;
+  }
+  // tile t (0 .. ntot-1): query head g*G + t / ntq, rows (t_first + t % ntq) * BR ..
+  auto tile_head = [&](int t) __attribute__((always_inline)) { return g * G + t / ntq; };
+  auto tile_row0 = [&](int t) __attribute__((always_inline)) { return (t_first + t % ntq) * BR; };
+  auto issue = [&](int t, const int BUF) __attribute__((always_inline)) {
+    const int hq = tile_head(t), r0 = tile_row0(t);
+    const size_t rb = (size_t)(b * a.H + hq) * a.Sq + r0;
+    const int bytes = max(a.Sq - r0, 0) * D * 2;
+    const __amdgpu_buffer_rsrc_t qr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + rb * D), (short)0, bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t dr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.dout + rb * D), (short)0, bytes, kBufferWord3);
+    uint16_t* qd = BUF ? q_lds1 : q_lds0;
+    uint16_t* dd = BUF ? d_lds1 : d_lds0;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      buffer_load_lds16(qr, qd + (wave * IPW + i) * 512, voff[i]);
+      buffer_load_lds16(dr, dd + (wave * IPW + i) * 512, voff[i]);
+    }
+    // LSE2 and D of the 64 rows (one dword per lane; rows past Sq read 0 and
+    // are masked)
+    if (wave < 2) {
+      const float* src = (wave == 0 ? a.lse2 : a.dsum) + rb;
+      const __amdgpu_buffer_rsrc_t sr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, max(a.Sq - r0, 0) * 4, kBufferWord3);
+      float* sd = BUF ? st_lds1[wave] : st_lds0[wave];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_void*)sd, 4, lane * 4, 0, 0, 0);
+    }
+  };
+  constexpr int kLoads = 2 * IPW;  // per wave per tile, plus one statistics load for waves 0 and 1
+
+  const int gq = lane >> 4, r4 = (lane >> 2) & 3, c4 = lane & 3;
+  uint32_t a_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) a_off[ks] = (n * D + (((ks * 2 + h) ^ k_swz<D>(n)) * 8)) * 2;
+  uint32_t tr_lo[NDB], tr_hi[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int dcol = 32 * db + 16 * (gq & 1) + 4 * c4;
+    const int rl = 4 * h + r4, rh = 8 + 4 * h + r4;
+    tr_lo[db] = (rl * D + (((dcol >> 3) ^ k_swz<D>(rl)) * 8) + (dcol & 7)) * 2;
+    tr_hi[db] = (rh * D + (((dcol >> 3) ^ k_swz<D>(rh)) * 8) + (dcol & 7)) * 2;
+  }
+
+  f32x16 dk[NDB], dv[NDB];  // dK^T, dV^T (rows: head dims; column: this lane's key)
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+
+  // P and dS of one 32-row block as bf16 B operands (step st holds rows
+  // 8(r/4).. for r/4 in {2st, 2st+1}); only this part differs between masked
+  // and unmasked tiles
+  auto scores = [&](lds_cchar* qb_, lds_cchar* db_, const float* st_l, const float* st_d, int r0, int blk32,
+                    u32x4 (&pp)[2], u32x4 (&dsp)[2], const bool MASKED) __attribute__((always_inline)) {
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 qa = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(qb_ + a_off[ks] + blk32 * 32 * D * 2);
+      const u32x4 da = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(db_ + a_off[ks] + blk32 * 32 * D * 2);
+      s = mfma_32x32x16_bf16(qa, kf[ks], s);
+      dp = mfma_32x32x16_bf16(da, vf[ks], dp);
+    }
+    // register r: query row r0 + 32 blk32 + 8(r/4) + 4h + r%4; this lane's key
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int rr = 32 * blk32 + 8 * rg + 4 * h;  // first of four consecutive rows
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(st_l + rr);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(st_d + rr);
+      float pv[4], dsv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * rg + e;
+        float p = fast_exp2(fmaf(s[r], a.c2, -l4[e]));
+        if (MASKED) {
+          const int qrow = r0 + rr + e;
+          const bool vis = qrow < a.Sq && key_ok && (!CAUSAL || key <= qrow + shift);
+          p = vis ? p : 0.f;
+        }
+        pv[e] = p;
+        dsv[e] = p * (dp[r] - d4[e]);
+      }
+      pp[rg >> 1][(rg & 1) * 2 + 0] = pack_bf16x2(pv[0], pv[1]);
+      pp[rg >> 1][(rg & 1) * 2 + 1] = pack_bf16x2(pv[2], pv[3]);
+      dsp[rg >> 1][(rg & 1) * 2 + 0] = pack_bf16x2(dsv[0], dsv[1]);
+      dsp[rg >> 1][(rg & 1) * 2 + 1] = pack_bf16x2(dsv[2], dsv[3]);
+    }
+  };
+
+  auto tile = [&](int t, const int BUF, const bool masked) __attribute__((always_inline)) {
+    lds_cchar* qb_ = (lds_cchar*)(BUF ? q_lds1 : q_lds0);
+    lds_cchar* db_ = (lds_cchar*)(BUF ? d_lds1 : d_lds0);
+    const float* st_l = BUF ? st_lds1[0] : st_lds0[0];
+    const float* st_d = BUF ? st_lds1[1] : st_lds0[1];
+    const int r0 = tile_row0(t);
+#pragma unroll
+    for (int blk32 = 0; blk32 < BR / 32; ++blk32) {
+      u32x4 pp[2], dsp[2];
+      if (masked)
+        scores(qb_, db_, st_l, st_d, r0, blk32, pp, dsp, true);
+      else
+        scores(qb_, db_, st_l, st_d, r0, blk32, pp, dsp, false);
+      // dV^T += dO^T P and dK^T += Q^T dS over the block's two 16-row steps
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int roff = (32 * blk32 + 16 * st) * D * 2;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const i16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(db_ + tr_lo[db] + roff));
+          const i16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(db_ + tr_hi[db] + roff));
+          const i16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(qb_ + tr_lo[db] + roff));
+          const i16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(qb_ + tr_hi[db] + roff));
+          u32x4 da, qa;
+          da[0] = __builtin_bit_cast(u32x2, dlo)[0];
+          da[1] = __builtin_bit_cast(u32x2, dlo)[1];
+          da[2] = __builtin_bit_cast(u32x2, dhi)[0];
+          da[3] = __builtin_bit_cast(u32x2, dhi)[1];
+          qa[0] = __builtin_bit_cast(u32x2, qlo)[0];
+          qa[1] = __builtin_bit_cast(u32x2, qlo)[1];
+          qa[2] = __builtin_bit_cast(u32x2, qhi)[0];
+          qa[3] = __builtin_bit_cast(u32x2, qhi)[1];
+          dv[db] = mfma_32x32x16_bf16(da, pp[st], dv[db]);
+          dk[db] = mfma_32x32x16_bf16(qa, dsp[st], dk[db]);
+        }
+      }
+    }
+  };
+
+  if (ntot > 0) {
+    issue(0, 0);
+    for (int t = 0; t < ntot; t += 2) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int tt = t + u;
+        if (tt < ntot) {
+          if (tt + 1 < ntot) {
+            issue(tt + 1, u ^ 1);
+            if (wave < 2)
+              wait_vmem_at_most<kLoads + 1>();
+            else
+              wait_vmem_at_most<kLoads>();
+          } else {
+            wait_vmem_all();
+          }
+          __syncthreads();
+          const int r0 = tile_row0(tt);
+          const bool full = r0 >= row_full && r0 + BR <= a.Sq && wk0 + 32 <= a.Sk;
+          tile(tt, u, !full);
+          __syncthreads();
+        }
+      }
+    }
+  }
+
+  if (key_ok) {
+    const size_t ko = ((size_t)(b * a.Hkv + g) * a.Sk + key) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int c = 32 * db + 8 * rg + 4 * h;
+        const uint32_t k0w = pack_bf16x2(dk[db][4 * rg + 0] * a.scale, dk[db][4 * rg + 1] * a.scale);
+        const uint32_t k1w = pack_bf16x2(dk[db][4 * rg + 2] * a.scale, dk[db][4 * rg + 3] * a.scale);
+        *reinterpret_cast<u32x2*>(a.dk + ko + c) = u32x2{k0w, k1w};
+        const uint32_t v0w = pack_bf16x2(dv[db][4 * rg + 0], dv[db][4 * rg + 1]);
+        const uint32_t v1w = pack_bf16x2(dv[db][4 * rg + 2], dv[db][4 * rg + 3]);
+        *reinterpret_cast<u32x2*>(a.dv + ko + c) = u32x2{v0w, v1w};
+      }
+  }
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+template <int D, bool CAUSAL>
+hipError_t launch(const BwdArgs& p, hipStream_t s) {
+  BwdKArgs a;
+  const size_t rows = (size_t)p.B * p.H * p.Sq;
+  a.q = static_cast<const uint16_t*>(p.q);
+  a.k = static_cast<const uint16_t*>(p.k);
+  a.v = static_cast<const uint16_t*>(p.v);
+  a.o = static_cast<const uint16_t*>(p.o);
+  a.dout = static_cast<const uint16_t*>(p.dout);
+  a.lse = p.lse;
+  a.lse2 = static_cast<float*>(p.workspace);
+  a.dsum = reinterpret_cast<float*>(static_cast<char*>(p.workspace) + align_up(rows * 4));
+  a.dq = static_cast<uint16_t*>(p.dq);
+  a.dk = static_cast<uint16_t*>(p.dk);
+  a.dv = static_cast<uint16_t*>(p.dv);
+  a.B = p.B;
+  a.H = p.H;
+  a.Hkv = p.Hkv;
+  a.Sq = p.Sq;
+  a.Sk = p.Sk;
+  a.nqb = (p.Sq + 127) / 128;
+  a.nkb = (p.Sk + 127) / 128;
+  a.c2 = p.scale * kLog2e;
+  a.scale = p.scale;
+  if (rows > 0) {
+    constexpr int rows_per_wg = kThreads / (D / 8);
+    hipLaunchKernelGGL((bwd_pre<D>), dim3((unsigned)((rows + rows_per_wg - 1) / rows_per_wg)), dim3(kThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dq<D, CAUSAL>), dim3((unsigned)((size_t)p.B * p.H * a.nqb)), dim3(kThreads), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if ((size_t)p.B * p.Hkv * p.Sk > 0) {
+    hipLaunchKernelGGL((bwd_dkdv<D, CAUSAL>), dim3((unsigned)((size_t)p.B * p.Hkv * a.nkb)), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int B, int H, int Sq) {
+  const size_t rows = (size_t)B * H * Sq;
+  return align_up(rows * 4) * 2;
+}
+
+hipError_t launch_bwd_bf16(const BwdArgs& p, hipStream_t s) {
+  if (p.d == 128) return p.causal ? launch<128, true>(p, s) : launch<128, false>(p, s);
+  return p.causal ? launch<64, true>(p, s) : launch<64, false>(p, s);
+}
+
+}  // namespace attn

@@ -47,15 +47,33 @@ struct SpecAcceptArgs {
   void* workspace;
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, H, Hkv, Sq, Sk, d;
+  int causal;
+  float scale;
+  void* workspace;
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_verify_bf16(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_spec_accept(const SpecAcceptArgs& a, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
 
 // Workgroups of the verify split kernel and the workspace it needs.
 int verify_split_workgroups();
 size_t verify_workspace_bytes(int B, int H, int Hkv, int kq, int d);
 size_t spec_accept_workspace_bytes(int B, int V);
+size_t bwd_workspace_bytes(int B, int H, int Sq);
 
 }  // namespace attn

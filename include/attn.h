@@ -174,6 +174,41 @@ int attn_verify_paged(const void* q, const void* k_pages, const void* v_pages,
                       void* stream);
 
 /*
+ * attn_bwd_workspace_bytes -- bytes of device workspace attn_bwd needs: two
+ * fp32 values per query row (rowsum(dO * O) and the base-2 LSE), each array
+ * aligned to 256 bytes.  Returns 0 for invalid sizes.
+ */
+size_t attn_bwd_workspace_bytes(int B, int H, int Sq);
+
+/*
+ * attn_bwd -- gradients of exact attention with respect to Q, K and V for an
+ * upstream gradient dO of its output ("Warmup Guide -- Inference
+ * Optimization at Depth", Ch.4, backward pass: P is recomputed from Q, K and
+ * the forward pass's per-row statistics instead of being stored).  With
+ * S = scale Q K^T (masked as in attn_fwd), P = softmax(S), O = P V:
+ *   dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dO * O)),
+ *   dQ = scale dS K, dK = scale dS^T Q;
+ * grouped-query heads sum into the dK, dV of their KV head.
+ *
+ *   q, o, dout   [B, H, Sq, d]     bf16 (read; o and lse as written by attn_fwd)
+ *   k, v         [B, Hkv, Sk, d]   bf16 (read)
+ *   lse          [B, H, Sq]        fp32 (read; natural log, -inf for empty rows)
+ *   dq           [B, H, Sq, d]     bf16 (written)
+ *   dk, dv       [B, Hkv, Sk, d]   bf16 (written)
+ *   workspace    attn_bwd_workspace_bytes(B, H, Sq) bytes, 16-byte aligned
+ *
+ * Accumulation is fp32; the outputs are rounded to bf16 (nearest even).
+ * Rows that see no key get dQ = 0 and contribute nothing to dK, dV.  Keys no
+ * query sees get dK = dV = 0.  No atomics: results are deterministic.
+ * dtype must be ATTN_BF16; d in {64, 128}; causal is bottom-right aligned.
+ * Errors as for attn_fwd, plus ATTN_ERR_WORKSPACE.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, int Sq,
+             int Sk, int d, int causal, float scale, int dtype, void* workspace,
+             size_t workspace_bytes, void* stream);
+
+/*
  * attn_spec_accept_workspace_bytes -- bytes of device workspace
  * attn_spec_accept needs: two int64 sums per (sequence, 4096-entry chunk of
  * the vocabulary).  Returns 0 for invalid sizes.

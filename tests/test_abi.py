@@ -232,3 +232,53 @@ def test_spec_accept_workspace_and_noop():
     assert call_spec(B=0, x=None, q=None, p=None, ua=None, us=None, n=None, out=None, ws=None) == bd.ATTN_OK
     # k = 0 needs no draft arrays
     assert call_spec(k=0, x=None, q=None, ua=None, wsb=0) == bd.ATTN_ERR_WORKSPACE
+
+
+def call_bwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, H=4, Hkv=2, Sq=16,
+             Sk=16, d=128, causal=1, scale=0.088, dtype=bd.ATTN_BF16, ws=FAKE, wsb=None, stream=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = bd.attn_bwd_workspace_bytes(a["B"], a["H"], a["Sq"])
+    return bd.attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["B"], a["H"],
+                       a["Hkv"], a["Sq"], a["Sk"], a["d"], a["causal"], a["scale"], a["dtype"], a["ws"], a["wsb"],
+                       a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(k=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(v=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(o=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(do=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(lse=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(lse=FAKE + 2), bd.ATTN_ERR_INVALID_ARG),
+    (dict(dq=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(dk=FAKE + 8), bd.ATTN_ERR_INVALID_ARG),
+    (dict(dv=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(ws=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(ws=FAKE + 4), bd.ATTN_ERR_INVALID_ARG),
+    (dict(wsb=16), bd.ATTN_ERR_WORKSPACE),
+    (dict(H=3), bd.ATTN_ERR_INVALID_ARG),
+    (dict(Hkv=0), bd.ATTN_ERR_INVALID_ARG),
+    (dict(Sq=-1), bd.ATTN_ERR_INVALID_ARG),
+    (dict(Sk=-1), bd.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), bd.ATTN_ERR_INVALID_ARG),
+    (dict(scale=0.0), bd.ATTN_ERR_INVALID_ARG),
+    (dict(d=96), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=bd.ATTN_F32), bd.ATTN_ERR_UNSUPPORTED),
+])
+def test_bwd_rejects(kw, code):
+    assert call_bwd(**kw) == code
+
+
+def test_bwd_workspace_and_noop():
+    # two 256-byte aligned fp32 arrays of B*H*Sq
+    assert bd.attn_bwd_workspace_bytes(1, 4, 16) == 2 * 256
+    assert bd.attn_bwd_workspace_bytes(2, 32, 8192) == 2 * 2 * 32 * 8192 * 4
+    assert bd.attn_bwd_workspace_bytes(1, 1, 65) == 2 * 512
+    assert bd.attn_bwd_workspace_bytes(0, 4, 16) == 0
+    assert bd.attn_bwd_workspace_bytes(-1, 4, 16) == 0
+    nothing = dict(q=None, k=None, v=None, o=None, do=None, lse=None, dq=None, dk=None, dv=None, ws=None)
+    assert call_bwd(B=0, **nothing) == bd.ATTN_OK
+    assert call_bwd(Sq=0, Sk=0, **nothing) == bd.ATTN_OK

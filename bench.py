@@ -22,7 +22,8 @@ After the timed steps, the entry points beyond the step are measured on the
 same verify workload, each against the HBM roofline ("extras"):
 attn_verify_paged (64-key pages in random physical order), attn_verify_tree
 (a random 5-node draft tree per sequence) and attn_spec_accept (8 sequences,
-k = 5, a 131072-entry vocabulary).
+k = 5, a 131072-entry vocabulary); and attn_bwd on the prefill workload
+against the bf16 matrix peak.
 """
 from __future__ import annotations
 
@@ -223,6 +224,30 @@ def extras(dev, wv, vq, caches, vsl, seqlens, max_len, stream) -> dict:
     return out
 
 
+def backward_leg(dev, wp, q, k, v, o, lse, stream) -> dict:
+    """attn_bwd on the prefill workload: the forward's O and LSE, a seeded
+    N(0,1) dO.  Algorithmic FLOPs: the five S-sized products (S, dP, dV, dQ,
+    dK) at 2*S*S*d each per head, halved for the causal mask -- 2.5 times the
+    forward's count; the kernels recompute S and dP once more, which is not
+    counted."""
+    import torch
+    from exact_attention_04_amd import binding, synth
+    do = synth.normal(np.random.default_rng(wp.seed + 1), (wp.B, wp.H, wp.Sq, wp.d), "bf16").to(dev)
+    ws = torch.empty(binding.attn_bwd_workspace_bytes(wp.B, wp.H, wp.Sq), dtype=torch.uint8, device=dev)
+
+    def bwd(i):
+        binding.bwd(q, k, v, o, lse, do, causal=True, scale=wp.scale, workspace=ws)
+    for i in range(3):
+        bwd(i)
+    us = timed_us(bwd, 10, stream)
+    flops = 2.5 * wp.flops()
+    tf = flops / (us.mean() * 1e-6) / 1e12
+    return {"workload": wp.name, "us_per_call": round(float(us.mean()), 1),
+            "algorithmic_flops": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+
+
 def profile_leg(args, dev) -> int:
     """Run one leg warmup+steps times with no timing or output (for rocprofv3)."""
     import torch
@@ -239,6 +264,13 @@ def profile_leg(args, dev) -> int:
         q, k, v = synth.prefill_inputs(w, dev)
         for _ in range(n):
             binding.fwd(q, k, v, causal=True, scale=w.scale)
+    elif args.only == "backward":
+        w = synth.CAUSAL_BF16_S8192
+        q, k, v = synth.prefill_inputs(w, dev)
+        o, lse = binding.fwd(q, k, v, causal=True, scale=w.scale)
+        do = synth.normal(np.random.default_rng(w.seed + 1), (w.B, w.H, w.Sq, w.d), "bf16").to(dev)
+        for _ in range(n):
+            binding.bwd(q, k, v, o, lse, do, causal=True, scale=w.scale)
     else:
         w = synth.VERIFY_BF16
         q, kc, vc, sl = synth.verify_inputs(w, dev)
@@ -257,7 +289,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "verify", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "verify", "backward", "copy"], default=None,
                     help="profiling aid: run just one leg (no JSON line); 'copy' runs a plain "
                          "1 GiB device-to-device copy used to calibrate the HBM byte counters")
     args = ap.parse_args()
@@ -362,6 +394,9 @@ def main() -> int:
     for name, e in out["extras"].items():
         log(f"{name}: {e['us_per_call']:.1f} us -> {e['roofline']['achieved']:.0f} GB/s "
             f"= {100 * e['roofline']['frac']:.1f}% of HBM")
+    out["extras"]["backward"] = b = backward_leg(dev, wp, q, k, v, o, lse, stream)
+    log(f"backward: {b['us_per_call'] / 1e3:.3f} ms -> {b['roofline']['achieved']:.1f} TFLOP/s "
+        f"= {100 * b['roofline']['frac']:.1f}% of bf16 peak")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wp)
     print(json.dumps(out), flush=True)

@@ -59,6 +59,17 @@ struct BwdKArgs {
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __builtin_bit_cast(float, x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __builtin_bit_cast(float, x & 0xffff0000u); }
 
+// 16-byte chunk position of a tile row in LDS (XOR swizzle) for tiles that
+// are read both ways: row-wise as A operands (16 consecutive rows, one
+// chunk each: the swizzle permutes the 16 chunk positions over any 16
+// consecutive rows) and by transpose reads (4 consecutive rows x 4
+// consecutive chunks: rows 4k..4k+3 differ in the swizzle's upper two bits).
+// Both patterns then touch all 64 banks once.
+template <int D>
+__device__ __forceinline__ int b_swz(int row) {
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+
 // ---- D = rowsum(dO * O) and the base-2 LSE, D/8 lanes per row
 template <int D>
 __global__ void __launch_bounds__(kThreads) bwd_pre(BwdKArgs a) {
@@ -138,12 +149,12 @@ bwd_dq(BwdKArgs a) {
     df[ks] = row_ok ? load16(dO + (size_t)row * D + ks * 16 + h * 8) : u32x4{0, 0, 0, 0};
   }
 
-  // HBM -> LDS loads (both tiles in the K layout: swizzle chunk ^ (row & 15))
+  // HBM -> LDS loads (both tiles in the b_swz layout)
   uint32_t voff[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
     const int r = (wave * IPW + i) * ROWS_PER_INSN + lane / CPR;
-    voff[i] = (r * D + (((lane % CPR) ^ k_swz<D>(r)) * 8)) * 2;
+    voff[i] = (r * D + (((lane % CPR) ^ b_swz<D>(r)) * 8)) * 2;
   }
   auto issue = [&](int t, const int BUF) __attribute__((always_inline)) {
     const int j0 = t * BC;
@@ -167,14 +178,14 @@ bwd_dq(BwdKArgs a) {
   const int gq = lane >> 4, r4 = (lane >> 2) & 3, c4 = lane & 3;
   uint32_t a_off[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) a_off[ks] = (n * D + (((ks * 2 + h) ^ k_swz<D>(n)) * 8)) * 2;
+  for (int ks = 0; ks < KS; ++ks) a_off[ks] = (n * D + (((ks * 2 + h) ^ b_swz<D>(n)) * 8)) * 2;
   uint32_t tr_lo[NDB], tr_hi[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
     const int dcol = 32 * db + 16 * (gq & 1) + 4 * c4;
     const int rl = 4 * h + r4, rh = 8 + 4 * h + r4;
-    tr_lo[db] = (rl * D + (((dcol >> 3) ^ k_swz<D>(rl)) * 8) + (dcol & 7)) * 2;
-    tr_hi[db] = (rh * D + (((dcol >> 3) ^ k_swz<D>(rh)) * 8) + (dcol & 7)) * 2;
+    tr_lo[db] = (rl * D + (((dcol >> 3) ^ b_swz<D>(rl)) * 8) + (dcol & 7)) * 2;
+    tr_hi[db] = (rh * D + (((dcol >> 3) ^ b_swz<D>(rh)) * 8) + (dcol & 7)) * 2;
   }
 
   f32x16 acc[NDB];
@@ -325,7 +336,7 @@ bwd_dkdv(BwdKArgs a) {
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
     const int r = (wave * IPW + i) * ROWS_PER_INSN + lane / CPR;
-    voff[i] = (r * D + (((lane % CPR) ^ k_swz<D>(r)) * 8)) * 2;
+    voff[i] = (r * D + (((lane % CPR) ^ b_swz<D>(r)) * 8)) * 2;
   }
   // tile t (0 .. ntot-1): query head g*G + t / ntq, rows (t_first + t % ntq) * BR ..
   auto tile_head = [&](int t) __attribute__((always_inline)) { return g * G + t / ntq; };
@@ -360,14 +371,14 @@ bwd_dkdv(BwdKArgs a) {
   const int gq = lane >> 4, r4 = (lane >> 2) & 3, c4 = lane & 3;
   uint32_t a_off[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) a_off[ks] = (n * D + (((ks * 2 + h) ^ k_swz<D>(n)) * 8)) * 2;
+  for (int ks = 0; ks < KS; ++ks) a_off[ks] = (n * D + (((ks * 2 + h) ^ b_swz<D>(n)) * 8)) * 2;
   uint32_t tr_lo[NDB], tr_hi[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
     const int dcol = 32 * db + 16 * (gq & 1) + 4 * c4;
     const int rl = 4 * h + r4, rh = 8 + 4 * h + r4;
-    tr_lo[db] = (rl * D + (((dcol >> 3) ^ k_swz<D>(rl)) * 8) + (dcol & 7)) * 2;
-    tr_hi[db] = (rh * D + (((dcol >> 3) ^ k_swz<D>(rh)) * 8) + (dcol & 7)) * 2;
+    tr_lo[db] = (rl * D + (((dcol >> 3) ^ b_swz<D>(rl)) * 8) + (dcol & 7)) * 2;
+    tr_hi[db] = (rh * D + (((dcol >> 3) ^ b_swz<D>(rh)) * 8) + (dcol & 7)) * 2;
   }
 
   f32x16 dk[NDB], dv[NDB];  // dK^T, dV^T (rows: head dims; column: this lane's key)

@@ -22,8 +22,9 @@ After the timed steps, the entry points beyond the step are measured on the
 same verify workload, each against the HBM roofline ("extras"):
 attn_verify_paged (64-key pages in random physical order), attn_verify_tree
 (a random 5-node draft tree per sequence) and attn_spec_accept (8 sequences,
-k = 5, a 131072-entry vocabulary); and attn_bwd on the prefill workload
-against the bf16 matrix peak.
+k = 5, a 131072-entry vocabulary); attn_bwd on the prefill workload
+against the bf16 matrix peak; and attn_fwd on the other prefill workloads
+(S = 2048 batch, S = 32768 at d = 128 and d = 64, the small fp32 case).
 """
 from __future__ import annotations
 
@@ -248,6 +249,35 @@ def backward_leg(dev, wp, q, k, v, o, lse, stream) -> dict:
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
 
 
+def other_prefill(dev, stream) -> dict:
+    """attn_fwd on the other prefill workloads (each timed alone, inputs
+    resident): the 2048-token batch, the 32768-token single sequences at
+    d = 128 and d = 64, and the small fp32 case (launch-bound: time only)."""
+    import torch
+    from exact_attention_04_amd import binding, synth
+    out = {}
+    for w in (synth.CAUSAL_BF16_S2048, synth.CAUSAL_BF16_S32768_D128, synth.CAUSAL_BF16_S32768_D64,
+              synth.NONCAUSAL_F32_S256):
+        q, k, v = synth.prefill_inputs(w, dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device=dev)
+
+        def call(i):
+            binding.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        for i in range(3):
+            call(i)
+        us = timed_us(call, 20, stream)
+        tf = w.flops() / (us.mean() * 1e-6) / 1e12
+        e = {"us_per_call": round(float(us.mean()), 2), "TFLOP/s": round(tf, 2)}
+        if w.dtype == "bf16":
+            e["roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}
+        out[w.name] = e
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+    return out
+
+
 def profile_leg(args, dev) -> int:
     """Run one leg warmup+steps times with no timing or output (for rocprofv3)."""
     import torch
@@ -397,6 +427,9 @@ def main() -> int:
     out["extras"]["backward"] = b = backward_leg(dev, wp, q, k, v, o, lse, stream)
     log(f"backward: {b['us_per_call'] / 1e3:.3f} ms -> {b['roofline']['achieved']:.1f} TFLOP/s "
         f"= {100 * b['roofline']['frac']:.1f}% of bf16 peak")
+    out["extras"]["prefill_other"] = po = other_prefill(dev, stream)
+    for name, e in po.items():
+        log(f"{name}: {e['us_per_call']:.1f} us -> {e['TFLOP/s']:.1f} TFLOP/s")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wp)
     print(json.dumps(out), flush=True)

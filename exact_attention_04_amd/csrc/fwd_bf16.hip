@@ -165,10 +165,28 @@ fwd_bf16_kernel(FwdKernelArgs a) {
   const bool lead = wave < 4;
   const int rb = 2 * (wave & 3) + (lead ? 0 : 1);
 
-  const int blk = xcd_grouped_block(blockIdx.x, gridDim.x);
-  const int bh = blk / a.nqb;
-  int qblk = blk - bh * a.nqb;
-  if (CAUSAL) qblk = a.nqb - 1 - qblk;  // heaviest query blocks of a head first
+  // Workgroup i runs on XCD i % 8, each XCD taking its ids in order.  Every
+  // XCD gets a contiguous range of heads.  When a head has at least as many
+  // query blocks as an XCD has CUs, the XCD runs its heads one after the
+  // other, heaviest block first (a head's blocks then share the XCD's L2);
+  // with fewer blocks per head (short sequences) the heads' blocks are
+  // interleaved, all heaviest blocks first, which keeps the causal tail
+  // balanced.
+  int bh, qblk;
+  {
+    constexpr int kXcds = 8, kCusPerXcd = 32;
+    const int nbh = gridDim.x / a.nqb;
+    if (CAUSAL && a.nqb < kCusPerXcd && nbh % kXcds == 0) {
+      const int x = blockIdx.x % kXcds, i = blockIdx.x / kXcds, hx = nbh / kXcds;
+      bh = x * hx + i % hx;
+      qblk = a.nqb - 1 - i / hx;
+    } else {
+      const int blk = xcd_grouped_block(blockIdx.x, gridDim.x);
+      bh = blk / a.nqb;
+      qblk = blk - bh * a.nqb;
+      if (CAUSAL) qblk = a.nqb - 1 - qblk;  // heaviest query blocks of a head first
+    }
+  }
   const int b = bh / a.H;
   const int hq = bh - b * a.H;
   const int g = hq / (a.H / a.Hkv);

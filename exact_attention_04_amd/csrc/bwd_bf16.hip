@@ -70,6 +70,18 @@ __device__ __forceinline__ int b_swz(int row) {
   return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
 }
 
+// Workgroup barrier for the tile hand-over: this wave's LDS reads have
+// completed, and no instruction is scheduled across it.  Unlike
+// __syncthreads() it does not wait for the HBM->LDS loads still in flight
+// (a workgroup fence would, and so would drain the prefetch of the next
+// tile); where a tile must have landed, vmcnt is waited for explicitly
+// first.
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---- D = rowsum(dO * O) and the base-2 LSE, D/8 lanes per row
 template <int D>
 __global__ void __launch_bounds__(kThreads) bwd_pre(BwdKArgs a) {
@@ -258,12 +270,12 @@ bwd_dq(BwdKArgs a) {
           } else {
             wait_vmem_all();
           }
-          __syncthreads();  // tile jj is in LDS for every wave
+          lds_sync();  // tile jj is in LDS for every wave
           if (jj < nfull)
             tile(jj, u, false);
           else
             tile(jj, u, true);
-          __syncthreads();  // everyone is done with buffer u before it is refilled
+          lds_sync();  // everyone is done with buffer u before it is refilled
         }
       }
     }
@@ -482,11 +494,11 @@ bwd_dkdv(BwdKArgs a) {
           } else {
             wait_vmem_all();
           }
-          __syncthreads();
+          lds_sync();
           const int r0 = tile_row0(tt);
           const bool full = r0 >= row_full && r0 + BR <= a.Sq && wk0 + 32 <= a.Sk;
           tile(tt, u, !full);
-          __syncthreads();
+          lds_sync();
         }
       }
     }

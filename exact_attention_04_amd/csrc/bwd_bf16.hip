@@ -17,11 +17,13 @@
 //       S^T = K Q^T, dP^T = V dO^T            (scores transposed: lane = query)
 //       dS^T = P^T * (dP^T - D)               (P^T = exp2(S^T c - LSE2))
 //       dQ^T += K^T dS^T                      (K^T by LDS transpose reads);
-//   * bwd_dkdv: one workgroup per (batch, KV head, 128 keys), each wave 32
-//     keys whose K and V rows it holds as MFMA B operands; it walks the query
-//     tiles of every query head that reads its KV head (grouped-query heads
-//     are summed here), Q/dO tiles and their D, LSE2 rows streaming through
-//     LDS, and per 32-row block
+//   * bwd_dkdv: one workgroup per (batch, KV head, 256 keys), eight waves
+//     (two per SIMD, so one wave's vector work overlaps the other's matrix
+//     work), each wave 32 keys: it holds their K rows as MFMA B operands and
+//     reads their V rows from LDS (dK/dV accumulators leave no registers for
+//     them); it walks the query tiles of every query head that reads its KV
+//     head (grouped-query heads are summed here), Q/dO tiles and their D,
+//     LSE2 rows streaming through LDS, and per 32-row block
 //       S = Q K^T, dP = dO V^T                (lane = key)
 //       dS = P * (dP - D)
 //       dV^T += dO^T P, dK^T += Q^T dS        (dO^T, Q^T by LDS transpose reads).
@@ -51,7 +53,7 @@ struct BwdKArgs {
   uint16_t* dv;
   int B, H, Hkv, Sq, Sk;
   int nqb;   // 128-row query blocks per (batch, head)
-  int nkb;   // 128-key blocks per (batch, KV head)
+  int nkb;   // key blocks of the dK/dV kernel per (batch, KV head)
   float c2;  // scale * log2(e)
   float scale;
 };
@@ -295,21 +297,31 @@ bwd_dq(BwdKArgs a) {
 }
 
 // ---- dK, dV
+#ifndef ATTN_BWD_KV_WAVES
+#define ATTN_BWD_KV_WAVES 8
+#endif
+constexpr int kKvWaves = ATTN_BWD_KV_WAVES;  // 4: one wave per SIMD, V in registers; 8: two, V in LDS
+constexpr int kKvThreads = 64 * kKvWaves;
+constexpr int kKvKeys = 32 * kKvWaves;       // keys per workgroup
+constexpr bool kVinLds = kKvWaves == 8;
+
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(kKvWaves / 4, kKvWaves / 4)))
 bwd_dkdv(BwdKArgs a) {
   constexpr int CPR = D / 8, KS = D / 16, NDB = D / 32;
   constexpr int BR = 64;  // query rows per tile
   constexpr int TILE = BR * D;
   constexpr int ROWS_PER_INSN = 1024 / (D * 2);
-  constexpr int IPW = TILE * 2 / 1024 / kWaves;
+  constexpr int IPW = TILE * 2 / 1024 / kKvWaves;
   static_assert(IPW >= 1, "every wave loads part of each tile");
+  constexpr int VIPW = kKvKeys * D * 2 / 1024 / kKvWaves;  // V rows of the workgroup into LDS
   __shared__ __attribute__((aligned(1024))) uint16_t q_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t q_lds1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t d_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t d_lds1[TILE];
   __shared__ __attribute__((aligned(256))) float st_lds0[2][BR];  // LSE2, D of the tile's rows
   __shared__ __attribute__((aligned(256))) float st_lds1[2][BR];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[kVinLds ? kKvKeys * D : 1];  // V rows k0 ..
   typedef const __attribute__((address_space(3))) char lds_cchar;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -320,18 +332,29 @@ bwd_dkdv(BwdKArgs a) {
   const int kblk = blk - bg * a.nkb;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int G = a.H / a.Hkv;
-  const int k0 = kblk * 128, wk0 = k0 + 32 * wave, shift = a.Sk - a.Sq;
+  const int k0 = kblk * kKvKeys, wk0 = k0 + 32 * wave, shift = a.Sk - a.Sq;
   const int key = wk0 + n;  // this lane's key
   const bool key_ok = key < a.Sk;
   const uint16_t* Kg = a.k + (size_t)(b * a.Hkv + g) * a.Sk * D;
   const uint16_t* Vg = a.v + (size_t)(b * a.Hkv + g) * a.Sk * D;
 
-  // K^T and V^T B operands of this lane's key
-  u32x4 kf[KS], vf[KS];
+  // K^T (and, with one wave per SIMD, V^T) B operands of this lane's key;
+  // with two waves per SIMD the V rows of the workgroup's keys go to LDS
+  // (rows past Sk read as zeros) and V^T is read from there
+  u32x4 kf[KS], vf[kVinLds ? 1 : KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     kf[ks] = key_ok ? load16(Kg + (size_t)key * D + ks * 16 + h * 8) : u32x4{0, 0, 0, 0};
-    vf[ks] = key_ok ? load16(Vg + (size_t)key * D + ks * 16 + h * 8) : u32x4{0, 0, 0, 0};
+    if constexpr (!kVinLds) vf[ks] = key_ok ? load16(Vg + (size_t)key * D + ks * 16 + h * 8) : u32x4{0, 0, 0, 0};
+  }
+  if constexpr (kVinLds) {
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Vg + (size_t)k0 * D), (short)0, max(a.Sk - k0, 0) * D * 2, kBufferWord3);
+#pragma unroll
+    for (int i = 0; i < VIPW; ++i) {
+      const int r = (wave * VIPW + i) * ROWS_PER_INSN + lane / CPR;
+      buffer_load_lds16(vr, v_lds + (wave * VIPW + i) * 512, (r * D + (((lane % CPR) ^ b_swz<D>(r)) * 8)) * 2);
+    }
   }
 
   // query tiles that see any of the workgroup's keys: rows i with
@@ -411,7 +434,17 @@ bwd_dkdv(BwdKArgs a) {
       const u32x4 qa = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(qb_ + a_off[ks] + blk32 * 32 * D * 2);
       const u32x4 da = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(db_ + a_off[ks] + blk32 * 32 * D * 2);
       s = mfma_32x32x16_bf16(qa, kf[ks], s);
-      dp = mfma_32x32x16_bf16(da, vf[ks], dp);
+      if constexpr (kVinLds) {
+        // row 32 wave + n of the V rows: its swizzle is that of n
+        const u32x4 vt = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            (lds_cchar*)v_lds + 32 * wave * D * 2 + a_off[ks]);
+        dp = mfma_32x32x16_bf16(da, vt, dp);
+      } else {
+        dp = mfma_32x32x16_bf16(da, vf[ks], dp);
+      }
+      // two waves per SIMD hide the LDS latency; keep the operands of one
+      // step live at a time
+      if constexpr (kVinLds) __builtin_amdgcn_sched_barrier(0);
     }
     // register r: query row r0 + 32 blk32 + 8(r/4) + 4h + r%4; this lane's key
 #pragma unroll
@@ -473,6 +506,7 @@ bwd_dkdv(BwdKArgs a) {
           qa[3] = __builtin_bit_cast(u32x2, qhi)[1];
           dv[db] = mfma_32x32x16_bf16(da, pp[st], dv[db]);
           dk[db] = mfma_32x32x16_bf16(qa, dsp[st], dk[db]);
+          if constexpr (kVinLds) __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
@@ -503,6 +537,8 @@ bwd_dkdv(BwdKArgs a) {
       }
     }
   }
+
+  wait_vmem_all();  // nothing may still be landing in LDS when the workgroup ends
 
   if (key_ok) {
     const size_t ko = ((size_t)(b * a.Hkv + g) * a.Sk + key) * D;
@@ -544,7 +580,7 @@ hipError_t launch(const BwdArgs& p, hipStream_t s) {
   a.Sq = p.Sq;
   a.Sk = p.Sk;
   a.nqb = (p.Sq + 127) / 128;
-  a.nkb = (p.Sk + 127) / 128;
+  a.nkb = (p.Sk + kKvKeys - 1) / kKvKeys;
   a.c2 = p.scale * kLog2e;
   a.scale = p.scale;
   if (rows > 0) {
@@ -557,7 +593,8 @@ hipError_t launch(const BwdArgs& p, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if ((size_t)p.B * p.Hkv * p.Sk > 0) {
-    hipLaunchKernelGGL((bwd_dkdv<D, CAUSAL>), dim3((unsigned)((size_t)p.B * p.Hkv * a.nkb)), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkdv<D, CAUSAL>), dim3((unsigned)((size_t)p.B * p.Hkv * a.nkb)), dim3(kKvThreads), 0, s,
+                       a);
     return hipGetLastError();
   }
   return hipSuccess;

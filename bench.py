@@ -246,7 +246,7 @@ def backward_leg(dev, wp, q, k, v, o, lse, stream) -> dict:
     return {"workload": wp.name, "us_per_call": round(float(us.mean()), 1),
             "algorithmic_flops": flops,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("backward")}}
 
 
 def other_prefill(dev, stream) -> dict:

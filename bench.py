@@ -19,12 +19,13 @@ every valid cache row plus Q, O and LSE, per call) rides along under
 the prefill workload (whole heads) on the host cores.
 
 After the timed steps, the entry points beyond the step are measured on the
-same verify workload, each against the HBM roofline ("extras"):
-attn_verify_paged (64-key pages in random physical order), attn_verify_tree
-(a random 5-node draft tree per sequence) and attn_spec_accept (8 sequences,
-k = 5, a 131072-entry vocabulary); attn_bwd on the prefill workload
-against the bf16 matrix peak; and attn_fwd on the other prefill workloads
-(S = 2048 batch, S = 32768 at d = 128 and d = 64, the small fp32 case).
+same verify workload, each against the HBM roofline ("extras"): attn_verify
+back to back (without the prefill before each call), attn_verify_paged
+(64-key pages in random physical order), attn_verify_tree (a random 5-node
+draft tree per sequence) and attn_spec_accept (8 sequences, k = 5, a
+131072-entry vocabulary); attn_bwd on the prefill workload against the bf16
+matrix peak; and attn_fwd on the other prefill workloads (S = 2048 batch,
+S = 32768 at d = 128 and d = 64, the small fp32 case).
 """
 from __future__ import annotations
 
@@ -166,12 +167,25 @@ def extras(dev, wv, vq, caches, vsl, seqlens, max_len, stream) -> dict:
     rng = np.random.default_rng(7)
     vbytes = verify_algorithmic_bytes(wv, seqlens)
     out = {}
-    # paged verify: two page pools in different random orders, alternated
-    pools = [paged_copy(kc, vc, seqlens, 64, rng) for kc, vc in caches[:2]]
-    ws = torch.empty(binding.attn_verify_workspace_bytes(wv.B, wv.H, wv.Hkv, wv.kq, wv.d), dtype=torch.uint8,
-                     device=dev)
+    # plain verify, back to back (the timed step runs it right after the
+    # prefill kernel has written its 268 MB of O)
+    def plain(i):
+        kc, vc = caches[i % len(caches)]
+        binding.verify(vq, kc, vc, vsl, max_len, scale=wv.scale, out=o, lse=lse, workspace=ws)
     o = torch.empty_like(vq)
     lse = torch.empty((wv.B, wv.H, wv.kq), dtype=torch.float32, device=dev)
+    ws = torch.empty(binding.attn_verify_workspace_bytes(wv.B, wv.H, wv.Hkv, wv.kq, wv.d), dtype=torch.uint8,
+                     device=dev)
+    for i in range(5):
+        plain(i)
+    us = timed_us(plain, 50, stream)
+    out["verify_back_to_back"] = {"us_per_call": round(float(us.mean()), 2),
+                                  "roofline": {"bound": "hbm", "achieved": round(vbytes / us.mean() / 1e3, 1),
+                                               "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                               "frac": round(vbytes / us.mean() / 1e3 / PEAK_HBM_GBPS, 4),
+                                               "traffic": None}}
+    # paged verify: two page pools in different random orders, alternated
+    pools = [paged_copy(kc, vc, seqlens, 64, rng) for kc, vc in caches[:2]]
 
     def paged(i):
         kp, vp, table = pools[i % 2]

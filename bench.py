@@ -161,9 +161,29 @@ def spec_inputs(B, k, V, dev, seed=12):
     return [torch.from_numpy(a).to(dev) for a in (x, q, p, ua, us)]
 
 
-def extras(dev, wv, vq, caches, vsl, seqlens, max_len, stream) -> dict:
+def oracle_threads() -> int:
+    """Threads the oracle's BLAS calls may use in this process."""
+    from oracle import ref_attention as ref
+    try:
+        return int(os.environ.get("OMP_NUM_THREADS", ""))
+    except ValueError:
+        return ref.default_workers()
+
+
+def cpu_rate(fn, work: float, unit: str, sample: str) -> dict:
+    """The oracle as it is, timed once on the host: work / seconds."""
+    t0 = time.perf_counter()
+    fn()
+    dt = time.perf_counter() - t0
+    scale = 1e9 if unit == "GB/s" else 1e12
+    return {"value": round(work / dt / scale, 4), "unit": unit, "cores": oracle_threads(), "kind": "oracle",
+            "sample": f"{sample}; {dt:.2f} s wall"}
+
+
+def extras(dev, wv, vq, caches, vsl, seqlens, max_len, stream, cpu: bool = False) -> dict:
     import torch
-    from exact_attention_04_amd import binding
+    from exact_attention_04_amd import binding, synth
+    from_dev = synth.to_f64
     rng = np.random.default_rng(7)
     vbytes = verify_algorithmic_bytes(wv, seqlens)
     out = {}
@@ -184,6 +204,12 @@ def extras(dev, wv, vq, caches, vsl, seqlens, max_len, stream) -> dict:
                                                "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                                "frac": round(vbytes / us.mean() / 1e3 / PEAK_HBM_GBPS, 4),
                                                "traffic": None}}
+    if cpu:
+        from oracle import ref_attention as ref
+        qn, kn, vn = from_dev(vq), from_dev(caches[0][0]), from_dev(caches[0][1])
+        out["verify_back_to_back"]["cpu_baseline"] = cpu_rate(
+            lambda: ref.verify(qn, kn, vn, seqlens, wv.scale), vbytes, "GB/s",
+            f"the whole {wv.name} call (fp64, materialised rows), rated by the same algorithmic bytes")
     # paged verify: two page pools in different random orders, alternated
     pools = [paged_copy(kc, vc, seqlens, 64, rng) for kc, vc in caches[:2]]
 
@@ -199,6 +225,13 @@ def extras(dev, wv, vq, caches, vsl, seqlens, max_len, stream) -> dict:
                                         "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                         "frac": round(pbytes / us.mean() / 1e3 / PEAK_HBM_GBPS, 4),
                                         "traffic": None}}
+    if cpu:
+        kp, vp, table = pools[0]
+        kpn, vpn, tabn = from_dev(kp), from_dev(vp), table.cpu().numpy()
+        out["verify_paged"]["cpu_baseline"] = cpu_rate(
+            lambda: ref.verify_paged(qn, kpn, vpn, tabn, seqlens, 64, wv.scale), pbytes, "GB/s",
+            "the whole paged call: gather of the logical cache, then verify (fp64)")
+        del kpn, vpn
     del pools
     # tree verify: a random 5-node tree per sequence
     tm = torch.from_numpy(tree_masks(rng, wv.B, wv.kq)).to(dev)
@@ -214,6 +247,12 @@ def extras(dev, wv, vq, caches, vsl, seqlens, max_len, stream) -> dict:
                                        "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                        "frac": round(vbytes / us.mean() / 1e3 / PEAK_HBM_GBPS, 4),
                                        "traffic": None}}
+    if cpu:
+        tmn = tm.cpu().numpy()
+        out["verify_tree"]["cpu_baseline"] = cpu_rate(
+            lambda: ref.verify_tree(qn, kn, vn, seqlens, tmn, wv.scale), vbytes, "GB/s",
+            "the whole tree-verify call (fp64, explicit visibility per row)")
+        del qn, kn, vn
     # acceptance rule: 8 sequences, k = 5, V = 131072; two input copies
     B, k, V = wv.B, wv.kq, 131072
     sets = [spec_inputs(B, k, V, dev, seed) for seed in (12, 13)]
@@ -236,10 +275,16 @@ def extras(dev, wv, vq, caches, vsl, seqlens, max_len, stream) -> dict:
                                        "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                        "frac": round(sbytes / us.mean() / 1e3 / PEAK_HBM_GBPS, 4),
                                        "traffic": None}}
+    if cpu:
+        from oracle import ref_spec
+        xs, qs, ps, uas, uss = (t.cpu().numpy() for t in sets[0])
+        out["spec_accept"]["cpu_baseline"] = cpu_rate(
+            lambda: ref_spec.spec_accept(xs, qs, ps, uas, uss), float(sbytes), "GB/s",
+            "one call on the first input set (numpy; fixed-point sums in int64)")
     return out
 
 
-def backward_leg(dev, wp, q, k, v, o, lse, stream) -> dict:
+def backward_leg(dev, wp, q, k, v, o, lse, stream, cpu: bool = False) -> dict:
     """attn_bwd on the prefill workload: the forward's O and LSE, a seeded
     N(0,1) dO.  Algorithmic FLOPs: the five S-sized products (S, dP, dV, dQ,
     dK) at 2*S*S*d each per head, halved for the causal mask -- 2.5 times the
@@ -257,10 +302,19 @@ def backward_leg(dev, wp, q, k, v, o, lse, stream) -> dict:
     us = timed_us(bwd, 10, stream)
     flops = 2.5 * wp.flops()
     tf = flops / (us.mean() * 1e-6) / 1e12
-    return {"workload": wp.name, "us_per_call": round(float(us.mean()), 1),
-            "algorithmic_flops": flops,
-            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("backward")}}
+    out = {"workload": wp.name, "us_per_call": round(float(us.mean()), 1),
+           "algorithmic_flops": flops,
+           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("backward")}}
+    if cpu:
+        from oracle import ref_attention as ref
+        one = (slice(0, 1), slice(0, 1))
+        qn, kn, vn, dn = (synth.to_f64(t[one]) for t in (q, k, v, do))
+        out["cpu_baseline"] = cpu_rate(
+            lambda: ref.attention_backward(qn, kn, vn, dn, True, wp.scale), flops / (wp.B * wp.H), "TFLOP/s",
+            f"one (batch, head) pair of {wp.name}: all {wp.Sq} rows, fp64 materialised S, P, dP, dS; rated by "
+            f"that head's share of the algorithmic FLOPs")
+    return out
 
 
 def other_prefill(dev, stream) -> dict:
@@ -434,11 +488,11 @@ def main() -> int:
         "prefill_ms": round(float(pre_ms.mean()), 4),
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
-    out["extras"] = extras(dev, wv, vq, caches, vsl, seqlens, max_len, stream)
+    out["extras"] = extras(dev, wv, vq, caches, vsl, seqlens, max_len, stream, cpu=not args.no_cpu_baseline)
     for name, e in out["extras"].items():
         log(f"{name}: {e['us_per_call']:.1f} us -> {e['roofline']['achieved']:.0f} GB/s "
             f"= {100 * e['roofline']['frac']:.1f}% of HBM")
-    out["extras"]["backward"] = b = backward_leg(dev, wp, q, k, v, o, lse, stream)
+    out["extras"]["backward"] = b = backward_leg(dev, wp, q, k, v, o, lse, stream, cpu=not args.no_cpu_baseline)
     log(f"backward: {b['us_per_call'] / 1e3:.3f} ms -> {b['roofline']['achieved']:.1f} TFLOP/s "
         f"= {100 * b['roofline']['frac']:.1f}% of bf16 peak")
     out["extras"]["prefill_other"] = po = other_prefill(dev, stream)

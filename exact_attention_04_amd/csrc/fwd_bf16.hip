@@ -207,6 +207,12 @@ fwd_bf16_kernel(FwdKernelArgs a) {
   const int nkt = (kend + kBc - 1) / kBc;
   int nfull = a.Sk / kBc;
   if (CAUSAL) nfull = min(nfull, max(wq0 + shift + 1, 0) / kBc);
+  // tiles [0, nneed) hold keys some row of this wave sees; the workgroup's
+  // later tiles (causal diagonal) are hidden from all of its rows, so the
+  // wave skips their matrix and vector work (it still takes part in the
+  // loads and barriers)
+  int nneed = nkt;
+  if (CAUSAL) nneed = min(nkt, (max(min(wq0 + 31, a.Sq - 1) + shift + 1, 0) + kBc - 1) / kBc);
 
   // ---- direct HBM -> LDS tile loads.  Wave-wide instruction i of this wave
   // fills LDS bytes [1024*(wave*INSN_PER_WAVE+i), +1024); lane l's 16 bytes
@@ -433,14 +439,15 @@ fwd_bf16_kernel(FwdKernelArgs a) {
     const bool more = !MASKED || j + 1 < nkt;  // rounds of the plain loop always have a next tile
     if (LEAD) issue(j, P);
     prio_matrix();
-    if (more) scores((P + 1) % kStages);
-    accumulate(P);
+    // unmasked rounds always need both tiles (j + 1 < nfull <= nneed)
+    if (more && (!MASKED || j + 1 < nneed)) scores((P + 1) % kStages);
+    if (!MASKED || j < nneed) accumulate(P);
     if (!MASKED) matrix_schedule();
     prio_vector();
     if (!LEAD) wait_vmem_at_most<kInFlight>();
     lds_barrier();
     if (!LEAD) issue(j + 1, (P + 1) % kStages);
-    if (more) {
+    if (more && (!MASKED || j + 1 < nneed)) {
       if (MASKED && j + 1 >= nfull) mask((j + 1) * kBc);
       probabilities();
     }
@@ -458,13 +465,15 @@ fwd_bf16_kernel(FwdKernelArgs a) {
     for (int t = 0; t + 1 < kStages; ++t) issue_v(t, t);
     wait_vmem_all();
     lds_barrier();
-    scores(0);
-    if (0 >= nfull) mask(0);
-    if (LEAD) probabilities();
+    if (nneed > 0) {
+      scores(0);
+      if (0 >= nfull) mask(0);
+      if (LEAD) probabilities();
+    }
     lds_barrier();
     if (!LEAD) {
       issue(0, 0);
-      probabilities();
+      if (nneed > 0) probabilities();
       lds_barrier();
     }
     // Rounds j < nplain produce an S_{j+1} that needs no mask for this

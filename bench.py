@@ -30,6 +30,7 @@ S = 32768 at d = 128 and d = 64, the small fp32 case).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -210,6 +211,30 @@ def extras(dev, wv, vq, caches, vsl, seqlens, max_len, stream, cpu: bool = False
         out["verify_back_to_back"]["cpu_baseline"] = cpu_rate(
             lambda: ref.verify(qn, kn, vn, seqlens, wv.scale), vbytes, "GB/s",
             f"the whole {wv.name} call (fp64, materialised rows), rated by the same algorithmic bytes")
+    # the same shape on the other seeds' length mixes (each rotated over
+    # four cache copies like the timed step); seed 0's 205 MB would fit in
+    # the last-level cache without the rotation
+    sweep = {}
+    for seed in (0, 1, 2, 3):
+        w = dataclasses.replace(wv, seed=seed, name=f"{wv.name}_seed{seed}")
+        sq, sk, sv, ssl = synth.verify_inputs(w, dev)
+        slen = ssl.cpu().numpy()
+        rot = [(sk, sv)] + [(sk.clone(), sv.clone()) for _ in range(3)]
+
+        def seeded(i):
+            kc, vc = rot[i % len(rot)]
+            binding.verify(sq, kc, vc, ssl, int(slen.max()), scale=w.scale, out=o, lse=lse, workspace=ws)
+        for i in range(5):
+            seeded(i)
+        us = timed_us(seeded, 50, stream)
+        sb = verify_algorithmic_bytes(w, slen)
+        sweep[f"seed{seed}"] = {"sum_seqlens": int(slen.sum()), "algorithmic_bytes": int(sb),
+                                "us_per_call": round(float(us.mean()), 2),
+                                "GB/s": round(sb / us.mean() / 1e3, 1),
+                                "frac": round(sb / us.mean() / 1e3 / PEAK_HBM_GBPS, 4)}
+        del sq, sk, sv, ssl, rot
+        torch.cuda.empty_cache()
+    out["verify_seeds"] = sweep
     # paged verify: two page pools in different random orders, alternated
     pools = [paged_copy(kc, vc, seqlens, 64, rng) for kc, vc in caches[:2]]
 
@@ -490,6 +515,10 @@ def main() -> int:
     }
     out["extras"] = extras(dev, wv, vq, caches, vsl, seqlens, max_len, stream, cpu=not args.no_cpu_baseline)
     for name, e in out["extras"].items():
+        if name == "verify_seeds":
+            for sd, r in e.items():
+                log(f"verify {sd}: {r['us_per_call']:.1f} us -> {r['GB/s']:.0f} GB/s = {100 * r['frac']:.1f}% of HBM")
+            continue
         log(f"{name}: {e['us_per_call']:.1f} us -> {e['roofline']['achieved']:.0f} GB/s "
             f"= {100 * e['roofline']['frac']:.1f}% of HBM")
     out["extras"]["backward"] = b = backward_leg(dev, wp, q, k, v, o, lse, stream, cpu=not args.no_cpu_baseline)

@@ -452,14 +452,14 @@ struct MergeArgs {
 };
 
 // One wave per (b, query head, new token).  The split kernel recorded how
-// many pieces the row's segment has; the wave then issues every load it needs
-// at once (one piece LSE per lane, eight piece outputs per round), reduces
-// the LSEs and accumulates its head dims with the broadcast weights
-// exp2(LSE_p - LSE).
+// many pieces the row's segment has; the wave loads that count, one piece LSE
+// per lane and eight piece outputs at once, reduces the LSEs and accumulates
+// its head dims with the broadcast weights exp2(LSE_p - LSE) (segments of
+// more than eight pieces take further rounds of loads).
 template <int D>
 __global__ void __launch_bounds__(256) verify_merge_kernel(MergeArgs a) {
   constexpr int EPL = D / 64;  // head dims per lane
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int lane = threadIdx.x & 63;
   const int total = a.B * a.H * a.kq;
   if (row >= total) return;
@@ -469,51 +469,42 @@ __global__ void __launch_bounds__(256) verify_merge_kernel(MergeArgs a) {
   const int g = hq / a.G, hh = hq - g * a.G;
   const int rn = hh * a.kq + qi;
   // pieces of the row's segment (0 for an empty one; nothing was written
-  // when the split kernel did not run)
-  const int nc = a.max_seqlen > 0 ? min(a.seg_np[b * a.Hkv + g], a.jmax) : 0;
+  // when the split kernel did not run).  The first piece LSE per lane and
+  // the first eight piece outputs are loaded before the count, so the common
+  // case costs one memory round trip; slots at or past the count (stale or
+  // never written) are loaded but never used.
   const size_t base = (size_t)(b * a.Hkv + g) * a.jmax;
+  const float lse_raw = a.part_lse[(base + min(lane, a.jmax - 1)) * a.R + rn];
+  float v[8][EPL];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float* src = a.part_o + ((base + min(k, a.jmax - 1)) * a.R + rn) * D + lane * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) v[k][e] = src[e];
+  }
+  const int np_raw = a.max_seqlen > 0 ? a.seg_np[b * a.Hkv + g] : 0;
+  const int nc = min(np_raw, a.jmax);
+  // the largest piece LSE: the first 64 pieces from the values loaded
+  // above, any others in further rounds
+  float M = lane < nc ? lse_raw : -INFINITY;
+  for (int c0 = 64; c0 < nc; c0 += 64)
+    M = fmaxf(M, (c0 + lane < nc) ? a.part_lse[(base + c0 + lane) * a.R + rn] : -INFINITY);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  const float M_use = (M == -INFINITY) ? 0.f : M;
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  float M = -INFINITY, L = 0.f;
-  if (nc <= 8) {
-    // common case: the LSE (one per lane) and all eight outputs at once
-    const float lse_l = (lane < nc) ? a.part_lse[(base + lane) * a.R + rn] : -INFINITY;
-    float v[8][EPL];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float* src = a.part_o + ((base + min(k, max(nc - 1, 0))) * a.R + rn) * D + lane * EPL;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) v[k][e] = nc > 0 ? src[e] : 0.f;
-    }
-    M = lse_l;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-    const float M_use = (M == -INFINITY) ? 0.f : M;
-    const float w = lane < nc ? fast_exp2(lse_l - M_use) : 0.f;
-    L = w;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float wk = __shfl(w, k, 64);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wk, v[k][e], acc[e]);
-    }
-  } else {
-    // pieces in rounds of 64 (one per lane)
-    const float lse_l = (lane < nc) ? a.part_lse[(base + lane) * a.R + rn] : -INFINITY;
-    M = lse_l;
-    for (int c0 = 64; c0 < nc; c0 += 64)
-      M = fmaxf(M, (c0 + lane < nc) ? a.part_lse[(base + c0 + lane) * a.R + rn] : -INFINITY);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-    const float M_use = (M == -INFINITY) ? 0.f : M;
-    for (int c0 = 0; c0 < nc; c0 += 64) {
-      const float x = c0 == 0 ? lse_l : ((c0 + lane < nc) ? a.part_lse[(base + c0 + lane) * a.R + rn] : -INFINITY);
-      const float w = (c0 + lane < nc) ? fast_exp2(x - M_use) : 0.f;
-      L += w;
-      const int cn = min(64, nc - c0);
-      for (int k0 = 0; k0 < cn; k0 += 8) {
-        float v[8][EPL];
+  float L = 0.f;
+  // pieces in rounds of 64 (one weight per lane), eight outputs at a time;
+  // the first eight are the ones loaded above
+  for (int c0 = 0; c0 < nc; c0 += 64) {
+    const float x = c0 == 0 ? lse_raw : ((c0 + lane < nc) ? a.part_lse[(base + c0 + lane) * a.R + rn] : -INFINITY);
+    const float w = (c0 + lane < nc) ? fast_exp2(x - M_use) : 0.f;
+    L += w;
+    const int cn = min(64, nc - c0);
+    for (int k0 = 0; k0 < cn; k0 += 8) {
+      if (c0 + k0 > 0) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const int kk = c0 + min(k0 + k, cn - 1);
@@ -521,12 +512,12 @@ __global__ void __launch_bounds__(256) verify_merge_kernel(MergeArgs a) {
 #pragma unroll
           for (int e = 0; e < EPL; ++e) v[k][e] = src[e];
         }
+      }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float wk = __shfl(w, min(k0 + k, 63), 64) * (k0 + k < cn ? 1.f : 0.f);
+      for (int k = 0; k < 8; ++k) {
+        const float wk = __shfl(w, min(k0 + k, 63), 64);
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wk, v[k][e], acc[e]);
-        }
+        for (int e = 0; e < EPL; ++e) acc[e] = k0 + k < cn ? fmaf(wk, v[k][e], acc[e]) : acc[e];
       }
     }
   }

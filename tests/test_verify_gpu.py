@@ -105,3 +105,43 @@ def test_verify_deterministic():
     o1, l1 = run_verify(q, k, v, sl, int(sl.max()), w.scale)
     o2, l2 = run_verify(q, k, v, sl, int(sl.max()), w.scale)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_verify_workspace_uninitialised_and_shared():
+    """The workspace needs no initialisation and may be shared by calls of
+    different shapes: starting from random bytes, and from all-ones bytes,
+    two workloads alternate on one workspace, and every call must equal the
+    first result of its workload bit for bit (a merge that used a stale piece
+    count or a slot its split did not write would change it)."""
+    from exact_attention_04_amd import binding
+    w = synth.VERIFY_BF16
+    qa, ka, va, sla = synth.verify_inputs(w, "cuda")
+    rng = np.random.default_rng(21)
+    lb = [700, 3000, 5, 1]
+    qb = synth.normal(rng, (4, 32, 4, 128), "bf16").cuda()
+    kb = synth.normal(rng, (4, 4, 3000, 128), "bf16").cuda()
+    vb = synth.normal(rng, (4, 4, 3000, 128), "bf16").cuda()
+    slb = torch.tensor(lb, dtype=torch.int32, device="cuda")
+    need = max(binding.attn_verify_workspace_bytes(8, 32, 8, 5, 128),
+               binding.attn_verify_workspace_bytes(4, 32, 4, 4, 128))
+    calls = [(qa, ka, va, sla, int(sla.max()), w.scale), (qb, kb, vb, slb, 3000, float(np.float32(128 ** -0.5)))]
+    refs = []
+    for q, k, v, sl, ml, sc in calls:
+        o, lse = binding.verify(q, k, v, sl, ml, scale=sc,
+                                workspace=torch.zeros(need, dtype=torch.uint8, device="cuda"))
+        refs.append((o.clone(), lse.clone()))
+    P.log("[verify] shared workspace: refs of two workloads done")
+    for fill in ("random", "ones"):
+        if fill == "random":
+            ws = torch.from_numpy(rng.integers(0, 256, need, dtype=np.uint8)).cuda()
+        else:
+            ws = torch.full((need,), 255, dtype=torch.uint8, device="cuda")
+        for it in range(12):
+            i = it % 2
+            q, k, v, sl, ml, sc = calls[i]
+            o, lse = binding.verify(q, k, v, sl, ml, scale=sc, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(o, refs[i][0]) and torch.equal(lse, refs[i][1]), (fill, it)
+    P.log("    ok 24 calls bitwise equal")
+    o, lse = refs[1]
+    check_verify(qb, kb, vb, np.array(lb), o, lse, float(np.float32(128 ** -0.5)), "shared-ws-b")

@@ -32,7 +32,10 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   const size_t nq = (size_t)B * H * Sq * d;
   const size_t nk = (size_t)B * Hkv * Sk * d;
   if (nq > kMaxElems || nk > kMaxElems) return ATTN_ERR_INVALID_ARG;
-  if ((size_t)B * H * (size_t)((Sq + 127) / 128) > 0x7fffffffu) return ATTN_ERR_INVALID_ARG;
+  // one workgroup per (batch, head, query block) must fit the grid: blocks
+  // of 256 rows (bf16) or 16 rows (fp32)
+  const size_t rows_per_block = dtype == ATTN_F32 ? 16 : 256;
+  if ((size_t)B * H * (((size_t)Sq + rows_per_block - 1) / rows_per_block) > 0x7fffffffu) return ATTN_ERR_INVALID_ARG;
   if (!ptr_ok(q, nq) || !ptr_ok(o, nq) || !ptr_ok(k, nk) || !ptr_ok(v, nk)) return ATTN_ERR_INVALID_ARG;
   if (lse != nullptr && !aligned4(lse)) return ATTN_ERR_INVALID_ARG;
   if (nq == 0) return ATTN_OK;

@@ -20,6 +20,7 @@
 //     streams its own steps HBM -> LDS with coalesced 16-byte
 //     buffer_load ... lds (one step ahead, two LDS stages per wave), so no
 //     wave ever waits for another and a CU keeps 64 KB of loads in flight;
+//     the loads are non-temporal, since every cache byte is read once;
 //   * S^T = K Q^T and O^T += V^T P^T on the 32x32x16 bf16 MFMA as in the
 //     prefill kernel (K as 16-byte LDS reads, V^T via transpose reads), with
 //     the same base-2 online softmax, lazily raised reference max and the
@@ -249,8 +250,8 @@ __global__ void __launch_bounds__(kThreads, 1) verify_split_kernel(SplitArgs a) 
       uint16_t* vd = ST ? v_st1[wave] : v_st0[wave];
 #pragma unroll
       for (int i = 0; i < INSN; ++i) {
-        buffer_load_lds16(kr, kd + i * 512, k_voff[i]);
-        buffer_load_lds16(vr, vd + i * 512, v_voff[i]);
+        buffer_load_lds16_stream(kr, kd + i * 512, k_voff[i]);
+        buffer_load_lds16_stream(vr, vd + i * 512, v_voff[i]);
       }
     };
 

@@ -404,17 +404,26 @@ bwd_dkdv(BwdKArgs a) {
   constexpr int kLoads = 2 * IPW;  // per wave per tile, plus one statistics load for waves 0 and 1
 
   const int gq = lane >> 4, r4 = (lane >> 2) & 3, c4 = lane & 3;
-  uint32_t a_off[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) a_off[ks] = (n * D + (((ks * 2 + h) ^ b_swz<D>(n)) * 8)) * 2;
-  uint32_t tr_lo[NDB], tr_hi[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const int dcol = 32 * db + 16 * (gq & 1) + 4 * c4;
+  // LDS byte offsets of the operand reads, one register each: the offset of
+  // step ks (row-wise reads) is a_off0 ^ 32 ks, that of head-dim block db
+  // (transpose reads) tr_lo0 / tr_hi0 ^ 64 db, because the swizzle only
+  // permutes chunk bits that the row term never sets.  Recomputing them at
+  // each use (one XOR) instead of holding 16 offsets keeps the kernel within
+  // its 256 registers: a spilled value is reloaded with a vector-memory load,
+  // and waiting for that reload would also wait for the next tile's loads.
+  uint32_t a_off0 = (n * D + ((h ^ b_swz<D>(n)) * 8)) * 2;
+  uint32_t tr_lo0, tr_hi0;
+  {
+    const int dcol = 16 * (gq & 1) + 4 * c4;
     const int rl = 4 * h + r4, rh = 8 + 4 * h + r4;
-    tr_lo[db] = (rl * D + (((dcol >> 3) ^ b_swz<D>(rl)) * 8) + (dcol & 7)) * 2;
-    tr_hi[db] = (rh * D + (((dcol >> 3) ^ b_swz<D>(rh)) * 8) + (dcol & 7)) * 2;
+    tr_lo0 = (rl * D + (((dcol >> 3) ^ b_swz<D>(rl)) * 8) + (dcol & 7)) * 2;
+    tr_hi0 = (rh * D + (((dcol >> 3) ^ b_swz<D>(rh)) * 8) + (dcol & 7)) * 2;
   }
+  // an opaque redefinition per block keeps the compiler from hoisting the
+  // sixteen XORs back out of the loop
+  auto refresh_offsets = [&]() __attribute__((always_inline)) {
+    asm volatile("" : "+v"(a_off0), "+v"(tr_lo0), "+v"(tr_hi0));
+  };
 
   f32x16 dk[NDB], dv[NDB];  // dK^T, dV^T (rows: head dims; column: this lane's key)
 #pragma unroll
@@ -431,13 +440,14 @@ bwd_dkdv(BwdKArgs a) {
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const u32x4 qa = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(qb_ + a_off[ks] + blk32 * 32 * D * 2);
-      const u32x4 da = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(db_ + a_off[ks] + blk32 * 32 * D * 2);
+      const uint32_t ao = a_off0 ^ (32 * ks);
+      const u32x4 qa = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(qb_ + ao + blk32 * 32 * D * 2);
+      const u32x4 da = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(db_ + ao + blk32 * 32 * D * 2);
       s = mfma_32x32x16_bf16(qa, kf[ks], s);
       if constexpr (kVinLds) {
         // row 32 wave + n of the V rows: its swizzle is that of n
         const u32x4 vt = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-            (lds_cchar*)v_lds + 32 * wave * D * 2 + a_off[ks]);
+            (lds_cchar*)v_lds + 32 * wave * D * 2 + ao);
         dp = mfma_32x32x16_bf16(da, vt, dp);
       } else {
         dp = mfma_32x32x16_bf16(da, vf[ks], dp);
@@ -480,6 +490,7 @@ bwd_dkdv(BwdKArgs a) {
     const int r0 = tile_row0(t);
 #pragma unroll
     for (int blk32 = 0; blk32 < BR / 32; ++blk32) {
+      refresh_offsets();
       u32x4 pp[2], dsp[2];
       if (masked)
         scores(qb_, db_, st_l, st_d, r0, blk32, pp, dsp, true);
@@ -491,10 +502,11 @@ bwd_dkdv(BwdKArgs a) {
         const int roff = (32 * blk32 + 16 * st) * D * 2;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const i16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(db_ + tr_lo[db] + roff));
-          const i16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(db_ + tr_hi[db] + roff));
-          const i16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(qb_ + tr_lo[db] + roff));
-          const i16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(qb_ + tr_hi[db] + roff));
+          const uint32_t tl = tr_lo0 ^ (64 * db), th = tr_hi0 ^ (64 * db);
+          const i16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(db_ + tl + roff));
+          const i16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(db_ + th + roff));
+          const i16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(qb_ + tl + roff));
+          const i16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(qb_ + th + roff));
           u32x4 da, qa;
           da[0] = __builtin_bit_cast(u32x2, dlo)[0];
           da[1] = __builtin_bit_cast(u32x2, dlo)[1];

@@ -139,3 +139,12 @@ def test_paged_full_workload_bitwise_equals_contiguous(page):
     assert torch.equal(o_p, o_c)
     assert torch.equal(l_p, l_c)
     check_paged(q, kp, vp, table, sl_h, page, o_p, l_p, w.scale, w.name)
+
+
+def test_paged_many_sequences():
+    """More than 64 sequences through the block table (lengths read 64 at a
+    time by the split kernel), some empty, with 32-key pages."""
+    rng = np.random.default_rng(91)
+    lengths = [int(x) for x in rng.integers(0, 500, 100)]
+    lengths[0] = lengths[64] = 0
+    paged_case(92, lengths, 8, 2, 4, 128, 32, what="paged-many-sequences")

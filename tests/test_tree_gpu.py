@@ -113,3 +113,11 @@ def test_tree_on_verify_workload():
     torch.cuda.synchronize()
     o_ref, l_ref = ref.verify_tree(synth.to_f64(q), synth.to_f64(k), synth.to_f64(v), sl_h, masks, w.scale)
     P.log(f"    ok {P.compare(synth.to_f64(o), synth.to_f64(lse), o_ref, l_ref, 'bf16', w.name)}")
+
+
+def test_tree_many_sequences():
+    """More than 64 sequences, each with its own random draft tree."""
+    rng = np.random.default_rng(93)
+    kq = 6
+    lengths = [int(x) for x in rng.integers(kq, 600, 90)]
+    tree_case(94, lengths, 8, 2, kq, 64, what="tree-many-sequences")

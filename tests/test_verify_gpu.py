@@ -145,3 +145,14 @@ def test_verify_workspace_uninitialised_and_shared():
     P.log("    ok 24 calls bitwise equal")
     o, lse = refs[1]
     check_verify(qb, kb, vb, np.array(lb), o, lse, float(np.float32(128 ** -0.5)), "shared-ws-b")
+
+
+def test_many_sequences():
+    """More than 64 sequences: the split kernel reads the lengths 64 at a
+    time (slice plan, segment walk, empty-sequence rows), so 150 ragged
+    sequences, some empty and some shorter than kq, cross those rounds."""
+    rng = np.random.default_rng(77)
+    lengths = [int(x) for x in rng.integers(0, 400, 150)]
+    for i in (0, 63, 64, 65, 127, 128, 149):
+        lengths[i] = int(rng.integers(0, 4))  # empty or fewer keys than queries
+    verify_case(78, lengths, 8, 2, 3, 128, what="many-sequences")

@@ -9,11 +9,12 @@
 //     dQ = scale dS K,   dK = scale dS^T Q,
 // with D_i = rowsum(dO_i * O_i), which equals sum_j P_ij dP_ij because O = P V.
 //
-// Three kernels, no atomics (deterministic):
-//   * bwd_pre: D_i and LSE_i * log2(e) per query row into the workspace;
+// Two kernels, no atomics (deterministic):
 //   * bwd_dq: one workgroup per (batch, head, 128 query rows), like the
 //     forward kernel: each wave holds 32 query rows' Q and dO as MFMA B
-//     operands, K/V tiles of 64 keys stream through LDS, and per tile
+//     operands, computes the rows' D_i and LSE_i * log2(e) (written to the
+//     workspace for the next kernel), K/V tiles of 64 keys stream through
+//     LDS, and per tile
 //       S^T = K Q^T, dP^T = V dO^T            (scores transposed: lane = query)
 //       dS^T = P^T * (dP^T - D)               (P^T = exp2(S^T c - LSE2))
 //       dQ^T += K^T dS^T                      (K^T by LDS transpose reads);
@@ -84,32 +85,6 @@ __device__ __forceinline__ void lds_sync() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// ---- D = rowsum(dO * O) and the base-2 LSE, D/8 lanes per row
-template <int D>
-__global__ void __launch_bounds__(kThreads) bwd_pre(BwdKArgs a) {
-  constexpr int LPR = D / 8;
-  const long long rows = (long long)a.B * a.H * a.Sq;
-  const long long row = (long long)blockIdx.x * (kThreads / LPR) + threadIdx.x / LPR;
-  const int sub = threadIdx.x % LPR;
-  const bool ok = row < rows;
-  float acc = 0.f;
-  if (ok) {
-    const u32x4 ov = load16(a.o + row * D + sub * 8);
-    const u32x4 dv = load16(a.dout + row * D + sub * 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc = fmaf(bf16_lo(ov[i]), bf16_lo(dv[i]), acc);
-      acc = fmaf(bf16_hi(ov[i]), bf16_hi(dv[i]), acc);
-    }
-  }
-#pragma unroll
-  for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (ok && sub == 0) {
-    a.dsum[row] = acc;
-    a.lse2[row] = a.lse[row] * kLog2e;  // -inf stays -inf
-  }
-}
-
 // ---- dQ
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -150,18 +125,32 @@ bwd_dq(BwdKArgs a) {
   int nfull = a.Sk / BC;  // tiles [0, nfull) need no mask for this wave's rows
   if (CAUSAL) nfull = min(nfull, max(wq0 + shift + 1, 0) / BC);
 
-  // per-lane row statistics; rows that see nothing get no gradient
-  const float lse2 = row_ok ? a.lse2[rbase + row] : -INFINITY;
-  const float dsum = row_ok ? a.dsum[rbase + row] : 0.f;
-  const bool live = lse2 != -INFINITY;
-  const float lse_use = live ? lse2 : 0.f;
-
-  u32x4 qf[KS], df[KS];  // Q^T and dO^T B operands (column = this lane's row)
+  // Q^T and dO^T B operands (column = this lane's row; the two halves of
+  // the wave hold alternate 8-value groups of the head dims), and the row
+  // statistics: D = rowsum(dO * O) from the same dO values and the matching
+  // O values, LSE2 = LSE * log2(e).  They are published for the dK/dV
+  // kernel, which runs next; rows that see nothing get no gradient.
+  u32x4 qf[KS], df[KS];
+  float dpart = 0.f;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     qf[ks] = row_ok ? load16(Q + (size_t)row * D + ks * 16 + h * 8) : u32x4{0, 0, 0, 0};
     df[ks] = row_ok ? load16(dO + (size_t)row * D + ks * 16 + h * 8) : u32x4{0, 0, 0, 0};
+    const u32x4 of = row_ok ? load16(a.o + (rbase + row) * D + ks * 16 + h * 8) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dpart = fmaf(bf16_lo(of[i]), bf16_lo(df[ks][i]), dpart);
+      dpart = fmaf(bf16_hi(of[i]), bf16_hi(df[ks][i]), dpart);
+    }
   }
+  const float dsum = sum_halves(dpart);
+  const float lse2 = row_ok ? a.lse[rbase + row] * kLog2e : -INFINITY;  // -inf stays -inf
+  if (row_ok && h == 0) {
+    a.dsum[rbase + row] = dsum;
+    a.lse2[rbase + row] = lse2;
+  }
+  const bool live = lse2 != -INFINITY;
+  const float lse_use = live ? lse2 : 0.f;
 
   // HBM -> LDS loads (both tiles in the b_swz layout)
   uint32_t voff[IPW];
@@ -596,12 +585,8 @@ hipError_t launch(const BwdArgs& p, hipStream_t s) {
   a.c2 = p.scale * kLog2e;
   a.scale = p.scale;
   if (rows > 0) {
-    constexpr int rows_per_wg = kThreads / (D / 8);
-    hipLaunchKernelGGL((bwd_pre<D>), dim3((unsigned)((rows + rows_per_wg - 1) / rows_per_wg)), dim3(kThreads), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dq<D, CAUSAL>), dim3((unsigned)((size_t)p.B * p.H * a.nqb)), dim3(kThreads), 0, s, a);
-    e = hipGetLastError();
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if ((size_t)p.B * p.Hkv * p.Sk > 0) {

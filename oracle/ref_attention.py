@@ -46,7 +46,10 @@ import numpy as np
 __all__ = [
     "visible_mask",
     "attention",
-    "attention_probs",
+    "attention_backward",
+    "verify_tree",
+    "gather_paged",
+    "verify_paged",
     "verify",
     "online_softmax_1d",
     "online_attention_row",
@@ -158,32 +161,6 @@ def attention(q, k, v, causal: bool, scale: float, rows: Optional[Sequence[int]]
         out[b, h] = o_bh
         lse[b, h] = l_bh
     return out, lse
-
-
-def attention_probs(q, k, causal: bool, scale: float) -> np.ndarray:
-    """The full probability matrix P [B, H, Sq, Sk] (tiny inputs only).
-
-    "Warmup Guide", Ch.1 step 2 with Ch.2's safe softmax; rows with no
-    visible key are all zero.
-    """
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    B, H, Sq, d = q.shape
-    Hkv, Sk = k.shape[1], k.shape[2]
-    group = H // Hkv
-    P = np.zeros((B, H, Sq, Sk), dtype=np.float64)
-    vis = visible_mask(Sq, Sk, causal)
-    for b in range(B):
-        for h in range(H):
-            s = scale * (q[b, h] @ k[b, h // group].T)
-            s = np.where(vis, s, -np.inf)
-            for i in range(Sq):
-                if not vis[i].any():
-                    continue
-                m = np.max(s[i])
-                e = np.exp(s[i] - m)
-                P[b, h, i] = e / np.sum(e)
-    return P
 
 
 def verify(q, k_cache, v_cache, seqlens_k, scale: float,
@@ -314,17 +291,19 @@ def verify_tree(q, k_cache, v_cache, seqlens_k, tree_mask, scale: float) -> Tupl
     return out, lse
 
 
-def gather_paged(pages, block_table, seqlens_k, page_size: int) -> np.ndarray:
-    """The logical cache [B, Hkv, max_len, d] held by a paged store.
+def gather_paged(pages, block_table, seqlens_k, page_size: int) -> Tuple[np.ndarray, np.ndarray]:
+    """The logical cache [B, Hkv, max_len, d] held by a paged store, and which
+    of its keys exist: present [B, max_len] bool.
 
     "Warmup Guide", Ch.8 (PagedAttention): KV storage is divided into
     fixed-size blocks of ``page_size`` tokens and each sequence holds a block
     table mapping its logical blocks to physical ones.  Logical key t of
     sequence b is therefore row t % page_size of physical page
     block_table[b][t // page_size].  pages: [num_pages, Hkv, page_size, d].
-    Rows at or past seqlens_k[b] are zero, and so are the rows of a block
-    whose table entry is not a valid page index (the library reads such a
-    block as zeros).
+    A table entry that is not a physical page index in [0, num_pages) maps its
+    logical block to no storage: the keys of that block do not exist (present
+    is False, their rows are left zero and must not be attended to).  Keys at
+    or past seqlens_k[b] are not present either.
     """
     pages = np.asarray(pages, dtype=np.float64)
     table = np.asarray(block_table)
@@ -335,6 +314,7 @@ def gather_paged(pages, block_table, seqlens_k, page_size: int) -> np.ndarray:
     B = len(sl)
     max_len = max(sl) if sl else 0
     out = np.zeros((B, Hkv, max_len, d), dtype=np.float64)
+    present = np.zeros((B, max_len), dtype=bool)
     for b in range(B):
         for blk in range((sl[b] + page_size - 1) // page_size):
             phys = int(table[b, blk])
@@ -342,17 +322,37 @@ def gather_paged(pages, block_table, seqlens_k, page_size: int) -> np.ndarray:
             n = min(page_size, sl[b] - t0)
             if 0 <= phys < num_pages:
                 out[b, :, t0:t0 + n] = pages[phys, :, :n]
-    return out
+                present[b, t0:t0 + n] = True
+    return out, present
 
 
 def verify_paged(q, k_pages, v_pages, block_table, seqlens_k, page_size: int, scale: float,
                  heads: Optional[Sequence[Tuple[int, int]]] = None) -> Tuple[np.ndarray, np.ndarray]:
-    """Speculative-verify attention over a paged KV cache: the logical cache
-    of ``gather_paged`` fed to ``verify`` (paging changes where K/V live,
-    not what attention computes)."""
-    k = gather_paged(k_pages, block_table, seqlens_k, page_size)
-    v = gather_paged(v_pages, block_table, seqlens_k, page_size)
-    return verify(q, k, v, seqlens_k, scale, heads=heads)
+    """Speculative-verify attention over a paged KV cache.
+
+    Paging changes where K/V live, not what attention computes: the logical
+    cache of ``gather_paged`` is attended to as in ``verify`` (query i of
+    sequence b sees keys [0, seqlens_k[b] - kq + i]), restricted to the keys
+    that exist.  A key in a block whose table entry names no page is absent,
+    exactly like a key past the sequence's length; a row left with no key
+    gets O = 0 and LSE = -inf.  ``heads`` restricts the work to those (b, h)
+    pairs (other outputs stay 0 / -inf).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, H, kq, d = q.shape
+    k, present = gather_paged(k_pages, block_table, seqlens_k, page_size)
+    v, _ = gather_paged(v_pages, block_table, seqlens_k, page_size)
+    G = H // k.shape[1]
+    sl = [int(x) for x in np.asarray(seqlens_k).reshape(-1)]
+    out = np.zeros((B, H, kq, v.shape[3]), dtype=np.float64)
+    lse = np.full((B, H, kq), -np.inf, dtype=np.float64)
+    todo = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+    for (b, h) in todo:
+        n = sl[b]
+        # the causal verify mask (bottom-right: Sq = kq, Sk = n) and presence
+        vis = visible_mask(kq, n, True) & present[b, :n][None, :]
+        out[b, h], lse[b, h] = _masked_head(q[b, h], k[b, h // G, :n], v[b, h // G, :n], vis, scale)
+    return out, lse
 
 
 def online_softmax_1d(x: Sequence[float], blocks: Iterable[int]) -> Tuple[float, float]:

@@ -93,12 +93,27 @@ def test_row_constant_shift_invariance(causal):
 # ---------------------------------------------------------------- pin 4
 @pytest.mark.parametrize("causal", [False, True])
 def test_probability_rows_sum_to_one(causal):
-    q, k = rnd(13, 2, 3, 9, 6) * 3, rnd(14, 2, 3, 9, 6)
-    P = ref.attention_probs(q, k, causal, 0.4)
-    np.testing.assert_allclose(P.sum(-1), 1.0, atol=1e-14 * 9)
+    """With V = I (one value dimension per key) the output of ``attention``
+    is P itself, so its rows are probability vectors: non-negative, summing
+    to one, zero above the causal diagonal.  They also agree with the LSE
+    output: P_ij = exp(s_ij - LSE_i)."""
+    B, H, Hkv, S, d, scale = 2, 4, 2, 9, 6, 0.4
+    q, k = rnd(13, B, H, S, d) * 3, rnd(14, B, Hkv, S, d)
+    eye = np.broadcast_to(np.eye(S), (B, Hkv, S, S)).copy()
+    P, lse = ref.attention(q, k, eye, causal, scale)
+    np.testing.assert_allclose(P.sum(-1), 1.0, atol=1e-14 * S)
     assert (P >= 0).all()
+    iu = np.triu_indices(S, 1)
     if causal:  # nothing above the diagonal
-        assert np.all(P[..., np.triu_indices(9, 1)[0], np.triu_indices(9, 1)[1]] == 0)
+        assert np.all(P[..., iu[0], iu[1]] == 0)
+    else:
+        assert np.all(P[..., iu[0], iu[1]] > 0)
+    for b in range(B):
+        for h in range(H):
+            s = scale * (q[b, h] @ k[b, h // (H // Hkv)].T)
+            vis = np.tril(np.ones((S, S), dtype=bool)) if causal else np.ones((S, S), dtype=bool)
+            np.testing.assert_allclose(np.where(vis, np.exp(s - lse[b, h][:, None]), 0.0), P[b, h],
+                                       rtol=1e-12, atol=1e-300)
 
 
 # ---------------------------------------------------------------- pin 5
@@ -441,21 +456,46 @@ def test_gather_paged_hand_example():
     """"Warmup Guide", Ch.8: logical key t of sequence b is row t % page of
     page table[b][t // page].  Pages of 2 tokens whose entries name their own
     (page, row); sequence 0 uses pages 2 then 0, sequence 1 shares page 1 for
-    both of its blocks (prefix sharing), sequence 2 has an invalid entry."""
+    both of its blocks (prefix sharing), sequence 2 has entries that name no
+    page (-1 and 7 >= num_pages), so its keys do not exist."""
     page, npg = 2, 3
     pages = np.zeros((npg, 1, page, 2))
     for p in range(npg):
         for r in range(page):
             pages[p, 0, r] = [p, r]
     table = np.array([[2, 0], [1, 1], [-1, 7]])
-    sl = [3, 4, 2]
-    got = ref.gather_paged(pages, table, sl, page)
+    sl = [3, 4, 4]
+    got, present = ref.gather_paged(pages, table, sl, page)
     expect0 = [[2, 0], [2, 1], [0, 0]]            # page 2 rows 0,1, then page 0 row 0
     expect1 = [[1, 0], [1, 1], [1, 0], [1, 1]]    # page 1 twice
     np.testing.assert_array_equal(got[0, 0, :3], expect0)
-    np.testing.assert_array_equal(got[0, 0, 3:], 0)  # past the length
     np.testing.assert_array_equal(got[1, 0], expect1)
-    np.testing.assert_array_equal(got[2], 0)  # invalid page index reads as zeros
+    np.testing.assert_array_equal(present, [[1, 1, 1, 0], [1, 1, 1, 1], [0, 0, 0, 0]])
+
+
+def test_verify_paged_absent_keys_hand_example():
+    """Keys of a block whose table entry names no page are absent: the result
+    is attention over the keys that exist, computed here by hand.  One query
+    head, kq = 2, d = 1, scale 1, pages of 2 keys.  Sequence 0 has 6 keys in
+    blocks [page 0, invalid, page 1]: keys 0,1 and 4,5 exist, 2,3 do not.
+    New token 0 (key 4) sees keys 0..4 -> {0, 1, 4}; new token 1 sees {0, 1, 4, 5}.
+    Sequence 1 has 2 keys, both new tokens, in an invalid block: its rows see
+    nothing, so O = 0 and LSE = -inf."""
+    page = 2
+    kp = np.zeros((2, 1, page, 1))
+    vp = np.zeros((2, 1, page, 1))
+    # logits q*k with q = 1: ln 1, ln 2 on page 0; ln 3, ln 4 on page 1
+    kp[0, 0, :, 0] = [np.log(1.0), np.log(2.0)]
+    kp[1, 0, :, 0] = [np.log(3.0), np.log(4.0)]
+    vp[0, 0, :, 0] = [10.0, 20.0]
+    vp[1, 0, :, 0] = [30.0, 40.0]
+    table = np.array([[0, -1, 1], [5, -1, -1]])
+    q = np.ones((2, 1, 2, 1))
+    o, lse = ref.verify_paged(q, kp, vp, table, [6, 2], page, 1.0)
+    # row 0: weights 1, 2, 3 on values 10, 20, 30; row 1: weights 1..4 on 10..40
+    np.testing.assert_allclose(o[0, 0, :, 0], [(10 + 40 + 90) / 6, (10 + 40 + 90 + 160) / 10], rtol=1e-14)
+    np.testing.assert_allclose(lse[0, 0], [np.log(6.0), np.log(10.0)], rtol=1e-14)
+    assert np.all(o[1] == 0) and np.all(np.isneginf(lse[1]))
 
 
 @pytest.mark.parametrize("page", [1, 4, 32])
@@ -463,7 +503,7 @@ def test_verify_paged_equals_contiguous_under_any_page_permutation(page):
     """Paging changes where K/V live, not the result: scatter a contiguous
     cache into randomly permuted pages (with spare pages full of NaN that no
     table entry names) and the paged oracle must give the contiguous result
-    exactly."""
+    up to summation order."""
     rng = np.random.default_rng(11)
     B, H, Hkv, kq, d = 3, 4, 2, 3, 8
     sl = np.array([37, 5, 64])
@@ -490,8 +530,11 @@ def test_verify_paged_equals_contiguous_under_any_page_permutation(page):
             vp[phys, :, :n] = v[b, :, blk * page:blk * page + n]
     o_c, l_c = ref.verify(q, k, v, sl, 0.4)
     o_p, l_p = ref.verify_paged(q, kp, vp, table, sl, page, 0.4)
-    np.testing.assert_array_equal(o_p, o_c)
-    np.testing.assert_array_equal(l_p, l_c)
+    assert np.all(ref.gather_paged(kp, table, sl, page)[1] == (np.arange(smax)[None, :] < sl[:, None]))
+    # the paged path applies the mask through an explicit visibility matrix,
+    # the contiguous one through ``attention``: equal up to summation order
+    np.testing.assert_allclose(o_p, o_c, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l_p, l_c, rtol=0, atol=1e-13)
 
 
 # ---------------------------------------------------------------- tree verify

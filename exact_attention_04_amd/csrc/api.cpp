@@ -75,7 +75,8 @@ int verify_contiguous(const void* q, const void* k_cache, const void* v_cache, c
   if (!scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  if ((H / Hkv) * kq > 32) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)(H / Hkv) * kq > 64) return ATTN_ERR_UNSUPPORTED;  // two 32-row query tiles at most
+  if (tree && kq > 32) return ATTN_ERR_UNSUPPORTED;                  // 32-bit visibility masks
   if ((long long)B * max_seqlen_k >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;  // total keys fit int32
   const size_t nq = (size_t)B * H * kq * d;
   const size_t nk = (size_t)B * Hkv * cache_stride * d;
@@ -146,12 +147,12 @@ extern "C" int attn_verify_paged(const void* q, const void* k_pages, const void*
   if (max_seqlen_k < 0 || max_blocks_per_seq < 0 || num_pages < 0) return ATTN_ERR_INVALID_ARG;
   int page_shift = 0;
   while (page_shift < 13 && (1 << page_shift) != page_size) ++page_shift;
-  if (page_size < 32 || page_size > 4096 || (1 << page_shift) != page_size) return ATTN_ERR_INVALID_ARG;
+  if (page_size < 16 || page_size > 4096 || (1 << page_shift) != page_size) return ATTN_ERR_INVALID_ARG;
   if ((long long)max_seqlen_k > (long long)max_blocks_per_seq * page_size) return ATTN_ERR_INVALID_ARG;
   if (!scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  if ((H / Hkv) * kq > 32) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)(H / Hkv) * kq > 64) return ATTN_ERR_UNSUPPORTED;  // two 32-row query tiles at most
   if ((long long)B * max_seqlen_k >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;  // total keys fit int32
   const size_t nq = (size_t)B * H * kq * d;
   const size_t nk = (size_t)num_pages * Hkv * page_size * d;

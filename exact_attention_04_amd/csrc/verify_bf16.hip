@@ -15,7 +15,8 @@
 // partial per piece.  Every CU thus streams the same number of K/V bytes
 // whatever the length mix of the batch.  Per piece:
 //   * the (H/Hkv)*kq query rows that read KV head g are packed into one
-//     32-row tile, so each K/V byte is read from HBM once;
+//     32-row tile (two when there are more than 32), so each K/V byte is
+//     read from HBM once;
 //   * the four waves take interleaved 32-key steps of the piece.  Each wave
 //     streams its own steps HBM -> LDS with coalesced 16-byte
 //     buffer_load ... lds (one step ahead, two LDS stages per wave), so no
@@ -31,11 +32,14 @@
 // wave step is 32 consecutive keys starting at a multiple of 32.  That lets
 // the same kernel read a paged cache ("Warmup Guide", Ch.8: fixed-size
 // blocks of tokens, a per-sequence block table from logical to physical
-// block): with a page size that is a multiple of 32, a step lies inside one
-// page, so the table is consulted once per step and each step's loads use
-// one buffer descriptor, as for the contiguous cache.  A wave keeps 64
-// consecutive table entries of its sequence in a VGPR (one per lane) and
-// picks a step's entry with readlane.
+// block): with a page size that is a power of two of at least 16 keys, each
+// 16-key half of a step lies inside one page, so the table is consulted once
+// per half step and each half's loads use one buffer descriptor, as for the
+// contiguous cache (for pages of 32 keys or more both halves name the same
+// page).  A wave keeps 64 consecutive table entries of its sequence in a
+// VGPR (one per lane) and picks an entry with readlane.  A table entry that
+// names no page (outside [0, num_pages)) means its keys do not exist: they
+// are masked like keys past the end of the sequence.
 // Merge kernel -- one wave per output row combines its segment's piece
 // partials (weights exp(LSE_p - LSE)) and writes O (bf16) and LSE (natural
 // log).
@@ -45,14 +49,11 @@
 namespace attn {
 namespace {
 
-#ifndef ATTN_VERIFY_WAVES
-#define ATTN_VERIFY_WAVES 4
-#endif
-#ifndef ATTN_VERIFY_WGS
-#define ATTN_VERIFY_WGS 256
-#endif
-constexpr int kSplitWgs = ATTN_VERIFY_WGS;  // slices of the key range (one workgroup each)
-constexpr int kWaves = ATTN_VERIFY_WAVES;
+// One workgroup per slice; MI355X has 256 compute units, so the split runs
+// in one round on the whole chip (on a partition with fewer units it simply
+// takes several).  Four waves share a workgroup's LDS.
+constexpr int kSplitWgs = 256;  // slices of the key range (one workgroup each)
+constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStep = 32;  // keys per wave step
 constexpr float kRescaleSlack = 8.0f;  // log2 units
@@ -81,10 +82,8 @@ __device__ __forceinline__ int clamp_len(int s, int max_len) { return min(max(s,
 // its P start-up units, then its L_s keys.  A workgroup that takes the start
 // of a second segment thus gets that many fewer keys, and all workgroups
 // finish together.
-#ifndef ATTN_VERIFY_PIECE_COST
-#define ATTN_VERIFY_PIECE_COST 512
-#endif
-constexpr int kPieceCost = ATTN_VERIFY_PIECE_COST;
+// (512 was measured best over a sweep of 0..1024.)
+constexpr int kPieceCost = 512;
 
 // Maximum pieces of one segment: a segment of L keys meets at most
 // L / T + 2 slices of length T = ceil(total_cost / kSplitWgs), and
@@ -119,7 +118,10 @@ __device__ __forceinline__ void slice_plan(const int32_t* seqlens, int B, int Hk
   T = (total + kSplitWgs - 1) / kSplitWgs;
 }
 
-template <int D, bool PAGED>
+// NS = 1 or 2 sets of 32 packed query rows: (H/Hkv)*kq <= 32 * NS.  With two
+// sets every K and V operand read from LDS feeds one MFMA per set, so the
+// cache is still streamed once per KV head.
+template <int D, bool PAGED, int NS>
 __global__ void __launch_bounds__(kThreads, 1) verify_split_kernel(SplitArgs a) {
   constexpr int KS = D / 16;
   constexpr int NDB = D / 32;
@@ -127,15 +129,18 @@ __global__ void __launch_bounds__(kThreads, 1) verify_split_kernel(SplitArgs a) 
   constexpr int STEP = kStep * D;              // elements per K (or V) stage
   constexpr int INSN = STEP * 2 / 1024;        // 1 KB HBM->LDS loads per stage
   constexpr int ROWS_PER_INSN = 1024 / (D * 2);
+  constexpr int HALF = kStep / 2;              // keys per half step (the smallest page)
+  static_assert(NS == 1 || NS == 2, "one or two 32-row query sets");
+  static_assert(HALF % ROWS_PER_INSN == 0, "a load instruction stays inside one half step");
   // Per wave: two stages of K and two of V, one LDS object per stage so the
   // compiler can tell the next step's loads from this step's reads.
   __shared__ __attribute__((aligned(1024))) uint16_t k_st0[kWaves][STEP];
   __shared__ __attribute__((aligned(1024))) uint16_t k_st1[kWaves][STEP];
   __shared__ __attribute__((aligned(1024))) uint16_t v_st0[kWaves][STEP];
   __shared__ __attribute__((aligned(1024))) uint16_t v_st1[kWaves][STEP];
-  __shared__ float red_m[kWaves][32];
-  __shared__ float red_l[kWaves][32];
-  __shared__ float red_lr[kWaves][32];
+  __shared__ float red_m[kWaves][32 * NS];
+  __shared__ float red_l[kWaves][32 * NS];
+  __shared__ float red_lr[kWaves][32 * NS];
 
   long long total, T;
   slice_plan(a.seqlens, a.B, a.Hkv, a.max_seqlen, total, T);
@@ -154,9 +159,16 @@ __global__ void __launch_bounds__(kThreads, 1) verify_split_kernel(SplitArgs a) 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
-  // packed row n = (query head g*G + n / kq, new token n % kq)
-  const bool row_ok = n < a.R;
-  const int hh = n / a.kq, qi = n - hh * a.kq;
+  // packed row 32*r + n of set r = (query head g*G + row / kq, new token row % kq)
+  bool row_ok[NS];
+  int hh[NS], qi[NS];
+#pragma unroll
+  for (int r = 0; r < NS; ++r) {
+    const int row = 32 * r + n;
+    row_ok[r] = row < a.R;
+    hh[r] = row / a.kq;
+    qi[r] = row - hh[r] * a.kq;
+  }
 
   // HBM->LDS: instruction i of a stage covers stage rows
   // [i*ROWS_PER_INSN, +ROWS_PER_INSN); lane l fills row i*ROWS_PER_INSN + l/CPR,
@@ -191,19 +203,24 @@ __global__ void __launch_bounds__(kThreads, 1) verify_split_kernel(SplitArgs a) 
     // set: the tokens before it for a chain (causal), its ancestors and
     // itself in a draft tree.
     const int nk0 = sk - a.kq;
-    uint32_t vis_new;
-    if (a.tree_mask != nullptr)
-      vis_new = row_ok ? a.tree_mask[(size_t)b * a.kq + qi] : 0u;
-    else
-      vis_new = (2u << qi) - 1u;  // qi < 32; 2u << 31 wraps to 0 and gives all ones
+    uint64_t vis_new[NS];
+#pragma unroll
+    for (int r = 0; r < NS; ++r) {
+      if (a.tree_mask != nullptr)
+        vis_new[r] = row_ok[r] ? a.tree_mask[(size_t)b * a.kq + qi[r]] : 0u;
+      else
+        vis_new[r] = (2ull << qi[r]) - 1ull;  // qi < 64; 2 << 63 wraps to 0 and gives all ones
+    }
     const uint16_t* Kb = a.k + (size_t)(b * a.Hkv + g) * a.cache_stride * D;
     const uint16_t* Vb = a.v + (size_t)(b * a.Hkv + g) * a.cache_stride * D;
 
-    u32x4 qf[KS];
-    {
-      const uint16_t* qrow = a.q + ((size_t)(b * a.H + g * a.G + hh) * a.kq + qi) * D;
+    u32x4 qf[NS][KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[ks] = row_ok ? load16(qrow + ks * 16 + h * 8) : u32x4{0, 0, 0, 0};
+    for (int r = 0; r < NS; ++r) {
+      const uint16_t* qrow = a.q + ((size_t)(b * a.H + g * a.G + hh[r]) * a.kq + qi[r]) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qf[r][ks] = row_ok[r] ? load16(qrow + ks * 16 + h * 8) : u32x4{0, 0, 0, 0};
     }
 
     // Paged cache: the wave's window of 64 block-table entries of sequence b
@@ -216,104 +233,143 @@ __global__ void __launch_bounds__(kThreads, 1) verify_split_kernel(SplitArgs a) 
       win = lp < a.max_blocks ? a.block_table[(size_t)b * a.max_blocks + lp] : -1;
       wait_vmem_all();
     };
+    // Which of a stage's 32 keys exist (bit i: key key0 + i).  A key in a
+    // block whose table entry names no page does not exist and is masked
+    // like a key past the piece; a contiguous cache has every key.
+    uint32_t present0 = 0xffffffffu, present1 = 0xffffffffu;
     // A step's buffer starts at its first key and ends at k1 (at most one
     // step): rows past the piece read as zero, and a step past the end reads
-    // nothing.  In a paged cache the step's rows are rows key0 % page.. of
-    // physical page table[key0 / page]; an entry outside [0, num_pages)
-    // reads as zeros.
+    // nothing.  In a paged cache each 16-key half of a step lies inside one
+    // page (pages hold a power of two >= 16 keys): its rows are rows
+    // key % page.. of physical page table[key / page], through a descriptor
+    // of its own whose base sits 16*hf rows before them, so the stage's
+    // per-lane offsets stay those of a contiguous step.
     auto issue = [&](int key0, const int ST) {
-      int bytes = max(min(k1 - key0, kStep), 0) * D * 2;
-      const uint16_t* kbase;
-      const uint16_t* vbase;
+      const int nk = max(min(k1 - key0, kStep), 0);  // keys of the step inside the piece
+      __amdgpu_buffer_rsrc_t kr[2], vr[2];
+      uint32_t present = 0xffffffffu;
       if constexpr (PAGED) {
-        size_t off = 0;
-        if (bytes > 0) {
-          const int page = key0 >> a.page_shift;
-          if (page < win0 || page >= win0 + 64) load_window(page);
-          const int phys = __builtin_amdgcn_readlane(win, page - win0);
-          if ((unsigned)phys < (unsigned)a.num_pages)
-            off = (((size_t)phys * a.Hkv + g) << a.page_shift) + (key0 & ((1 << a.page_shift) - 1));
-          else
-            bytes = 0;
+        const int p0 = key0 >> a.page_shift, p1 = (key0 + HALF) >> a.page_shift;
+        if (nk > 0 && (p0 < win0 || p1 >= win0 + 64)) load_window(p0);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int key = key0 + HALF * hf;
+          const int nh = max(min(nk - HALF * hf, HALF), 0);
+          const uint16_t* kbase = a.k;
+          const uint16_t* vbase = a.v;
+          int bytes = 0;
+          if (nh > 0) {
+            const int phys = __builtin_amdgcn_readlane(win, (key >> a.page_shift) - win0);
+            if ((unsigned)phys < (unsigned)a.num_pages) {
+              const size_t row0 = (((size_t)phys * a.Hkv + g) << a.page_shift) + (key & ((1 << a.page_shift) - 1));
+              kbase = a.k + (row0 - HALF * hf) * D;
+              vbase = a.v + (row0 - HALF * hf) * D;
+              bytes = (HALF * hf + nh) * D * 2;
+            } else {
+              present &= hf ? 0x0000ffffu : 0xffff0000u;
+            }
+          }
+          kr[hf] = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, bytes, kBufferWord3);
+          vr[hf] = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, bytes, kBufferWord3);
         }
-        kbase = a.k + off * D;
-        vbase = a.v + off * D;
       } else {
-        kbase = Kb + (size_t)key0 * D;
-        vbase = Vb + (size_t)key0 * D;
+        kr[0] = kr[1] = __builtin_amdgcn_make_buffer_rsrc((void*)(Kb + (size_t)key0 * D), (short)0, nk * D * 2,
+                                                          kBufferWord3);
+        vr[0] = vr[1] = __builtin_amdgcn_make_buffer_rsrc((void*)(Vb + (size_t)key0 * D), (short)0, nk * D * 2,
+                                                          kBufferWord3);
       }
-      const __amdgpu_buffer_rsrc_t kr =
-          __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, bytes, kBufferWord3);
-      const __amdgpu_buffer_rsrc_t vr =
-          __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, bytes, kBufferWord3);
+      if (ST)
+        present1 = present;
+      else
+        present0 = present;
       uint16_t* kd = ST ? k_st1[wave] : k_st0[wave];
       uint16_t* vd = ST ? v_st1[wave] : v_st0[wave];
 #pragma unroll
       for (int i = 0; i < INSN; ++i) {
-        buffer_load_lds16_stream(kr, kd + i * 512, k_voff[i]);
-        buffer_load_lds16_stream(vr, vd + i * 512, v_voff[i]);
+        const int hf = i * ROWS_PER_INSN >= HALF;
+        buffer_load_lds16_stream(kr[hf], kd + i * 512, k_voff[i]);
+        buffer_load_lds16_stream(vr[hf], vd + i * 512, v_voff[i]);
       }
     };
 
-    f32x16 acc_o[NDB];
+    f32x16 acc_o[NS][NDB];
+    float m_ref[NS], l_run[NS], l_rnd[NS];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
-    float m_ref = -INFINITY, l_run = 0.f, l_rnd = 0.f;
+    for (int r = 0; r < NS; ++r) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc_o[r][db] = f32x16{};
+      m_ref[r] = -INFINITY;
+      l_run[r] = 0.f;
+      l_rnd[r] = 0.f;
+    }
 
     auto compute = [&](int key0, const int ST) {
       lds_cchar* kt = (lds_cchar*)(ST ? k_st1[wave] : k_st0[wave]);
       lds_cchar* vt = (lds_cchar*)(ST ? v_st1[wave] : v_st0[wave]);
-      f32x16 s = f32x16{};
+      const uint32_t present = ST ? present1 : present0;
+      f32x16 s[NS];
+#pragma unroll
+      for (int r = 0; r < NS; ++r) s[r] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const u32x4 kf = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(kt + k_off[ks]);
-        s = mfma_32x32x16_bf16(kf, qf[ks], s);
+#pragma unroll
+        for (int r = 0; r < NS; ++r) s[r] = mfma_32x32x16_bf16(kf, qf[r][ks], s[r]);
       }
-      // mask among the new tokens, end of the piece: bit i of vis is set
-      // iff key key0 + i is visible to this lane's row (every key before
-      // nk0, new key nk0 + t iff bit t of vis_new, nothing from k1 on);
-      // register r holds key 4h + 8(r/4) + r%4 of the step
-      if (key0 + kStep - 1 >= nk0 || key0 + kStep > k1) {
+      // mask among the new tokens, end of the piece, absent keys: bit i of
+      // vis is set iff key key0 + i is visible to this lane's row (every key
+      // before nk0, new key nk0 + t iff bit t of vis_new, nothing from k1
+      // on, only keys that exist); register r holds key 4h + 8(r/4) + r%4 of
+      // the step
+      if (key0 + kStep - 1 >= nk0 || key0 + kStep > k1 || present != 0xffffffffu) {
         const int dn = nk0 - key0;  // step position of new key 0
         const int dk = k1 - key0;   // step positions [0, dk) are inside the piece
         const uint32_t old_keys = dn <= 0 ? 0u : (dn >= 32 ? 0xffffffffu : (1u << dn) - 1u);
-        const uint64_t shifted = dn >= 0 ? ((uint64_t)vis_new << min(dn, 32)) : ((uint64_t)vis_new >> min(-dn, 32));
         const uint32_t in_piece = dk <= 0 ? 0u : (dk >= 32 ? 0xffffffffu : (1u << dk) - 1u);
-        const uint32_t vis = ((old_keys | (uint32_t)shifted) & in_piece) >> (4 * h);
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          s[r] = ((vis >> (8 * (r / 4) + (r % 4))) & 1u) ? s[r] : -INFINITY;
+        for (int r = 0; r < NS; ++r) {
+          const uint64_t shifted = dn >= 0 ? (vis_new[r] << min(dn, 32)) : (-dn >= 64 ? 0ull : vis_new[r] >> -dn);
+          const uint32_t vis = ((old_keys | (uint32_t)shifted) & in_piece & present) >> (4 * h);
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            s[r][e] = ((vis >> (8 * (e / 4) + (e % 4))) & 1u) ? s[r][e] : -INFINITY;
+        }
       }
-      float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-      mx = max_halves(mx) * a.c2;
-      const bool raise = mx > m_ref + kRescaleSlack;
-      if (__builtin_expect(__any(raise), 0)) {
-        asm volatile("");
-        const float alpha = raise ? fast_exp2(m_ref - mx) : 1.f;  // 0 when m_ref = -inf
-        m_ref = raise ? mx : m_ref;
-        l_run *= alpha;
-        l_rnd *= alpha;
+      for (int r = 0; r < NS; ++r) {
+        float mx = -INFINITY;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[r][e]);
+        mx = max_halves(mx) * a.c2;
+        const bool raise = mx > m_ref[r] + kRescaleSlack;
+        if (__builtin_expect(__any(raise), 0)) {
+          asm volatile("");
+          const float alpha = raise ? fast_exp2(m_ref[r] - mx) : 1.f;  // 0 when m_ref = -inf
+          m_ref[r] = raise ? mx : m_ref[r];
+          l_run[r] *= alpha;
+          l_rnd[r] *= alpha;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
-      }
-      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+          for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = fast_exp2(fmaf(s[r], a.c2, -m_use));
-        l_run += s[r];
+            for (int e = 0; e < 16; ++e) acc_o[r][db][e] *= alpha;
+        }
+        const float m_use = (m_ref[r] == -INFINITY) ? 0.f : m_ref[r];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          s[r][e] = fast_exp2(fmaf(s[r][e], a.c2, -m_use));
+          l_run[r] += s[r][e];
+        }
       }
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        u32x4 pt;
+        u32x4 pt[NS];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          pt[w] = pack_bf16x2(s[8 * t + 2 * w], s[8 * t + 2 * w + 1]);
-          l_rnd = sum_bf16x2(pt[w], l_rnd);
-        }
+        for (int r = 0; r < NS; ++r)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            pt[r][w] = pack_bf16x2(s[r][8 * t + 2 * w], s[r][8 * t + 2 * w + 1]);
+            l_rnd[r] = sum_bf16x2(pt[r][w], l_rnd[r]);
+          }
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           lds_cchar* vb = vt + v_off[db] + 16 * t * D * 2;
@@ -324,7 +380,8 @@ __global__ void __launch_bounds__(kThreads, 1) verify_split_kernel(SplitArgs a) 
           vf[1] = __builtin_bit_cast(u32x2, lo4)[1];
           vf[2] = __builtin_bit_cast(u32x2, hi4)[0];
           vf[3] = __builtin_bit_cast(u32x2, hi4)[1];
-          acc_o[db] = mfma_32x32x16_bf16(vf, pt, acc_o[db]);
+#pragma unroll
+          for (int r = 0; r < NS; ++r) acc_o[r][db] = mfma_32x32x16_bf16(vf, pt[r], acc_o[r][db]);
         }
       }
     };
@@ -350,32 +407,38 @@ __global__ void __launch_bounds__(kThreads, 1) verify_split_kernel(SplitArgs a) 
     wait_vmem_all();  // the last (empty) loads are done before the stages are reused
 
     // ---- combine the waves through LDS.  Each wave parks its fp32
-    // accumulator [D][32] in its own two K stages (head dims < D/2 in stage 0,
-    // the rest in stage 1); no other wave touches them before the barrier.
-    auto red_at = [&](int w, int d) -> float* {
-      uint16_t* st = d < D / 2 ? k_st0[w] : k_st1[w];
+    // accumulator of set r, [D][32], in two of its own stages (set 0 in the
+    // K stages, set 1 in the V stages; head dims < D/2 in the first, the
+    // rest in the second); no other wave touches them before the barrier.
+    auto red_at = [&](int w, int r, int d) -> float* {
+      uint16_t* st = r == 0 ? (d < D / 2 ? k_st0[w] : k_st1[w]) : (d < D / 2 ? v_st0[w] : v_st1[w]);
       return reinterpret_cast<float*>(st) + (d % (D / 2)) * 32;
     };
-    static_assert(STEP * 2 >= (D / 2) * 32 * 4, "a K stage holds half of a wave's accumulator");
-    const float l_tot = sum_halves(l_run);
-    const float lr_tot = sum_halves(l_rnd);
-    if (h == 0) {
-      red_m[wave][n] = m_ref;
-      red_l[wave][n] = l_tot;
-      red_lr[wave][n] = lr_tot;
-    }
+    static_assert(STEP * 2 >= (D / 2) * 32 * 4, "a stage holds half of a wave's accumulator of one set");
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int d = 32 * db + 8 * (r / 4) + 4 * h + (r % 4);
-        red_at(wave, d)[n] = acc_o[db][r];
+    for (int r = 0; r < NS; ++r) {
+      const float l_tot = sum_halves(l_run[r]);
+      const float lr_tot = sum_halves(l_rnd[r]);
+      if (h == 0) {
+        red_m[wave][32 * r + n] = m_ref[r];
+        red_l[wave][32 * r + n] = l_tot;
+        red_lr[wave][32 * r + n] = lr_tot;
       }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int d = 32 * db + 8 * (e / 4) + 4 * h + (e % 4);
+          red_at(wave, r, d)[n] = acc_o[r][db][e];
+        }
+    }
     __syncthreads();
     {
-      const int rn = tid & 31;  // packed row
-      const int dg = tid >> 5;  // group of DPT head dims
-      constexpr int DPT = D / (kThreads / 32);
+      constexpr int ROWS = 32 * NS;
+      const int rn = tid % ROWS;  // packed row
+      const int rs = rn / 32, rl = rn % 32;
+      const int dg = tid / ROWS;  // group of DPT head dims
+      constexpr int DPT = D / (kThreads / ROWS);
       float M = -INFINITY;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w][rn]);
@@ -399,7 +462,7 @@ __global__ void __launch_bounds__(kThreads, 1) verify_split_kernel(SplitArgs a) 
           for (int u = 0; u < 4; ++u) {
             float acc = 0.f;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) acc = fmaf(f[w], red_at(w, dg * DPT + d4 + u)[rn], acc);
+            for (int w = 0; w < kWaves; ++w) acc = fmaf(f[w], red_at(w, rs, dg * DPT + d4 + u)[rl], acc);
             vv[u] = acc * inv;
           }
           *reinterpret_cast<f32x4*>(dst + d4) = vv;
@@ -539,7 +602,7 @@ __global__ void __launch_bounds__(256) verify_merge_kernel(MergeArgs a) {
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
-template <int D, bool PAGED>
+template <int D, bool PAGED, int NS>
 hipError_t launch(const VerifyArgs& p, hipStream_t s) {
   const int G = p.H / p.Hkv;
   const int R = G * p.kq;
@@ -574,7 +637,7 @@ hipError_t launch(const VerifyArgs& p, hipStream_t s) {
   sa.jmax = jmax;
   sa.c2 = p.scale * kLog2e;
   if (p.max_seqlen_k > 0) {
-    hipLaunchKernelGGL((verify_split_kernel<D, PAGED>), dim3(kSplitWgs), dim3(kThreads), 0, s, sa);
+    hipLaunchKernelGGL((verify_split_kernel<D, PAGED, NS>), dim3(kSplitWgs), dim3(kThreads), 0, s, sa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -609,9 +672,15 @@ size_t verify_workspace_bytes(int B, int H, int Hkv, int kq, int d) {
   return align_up(n_parts * d * 4) + align_up(n_parts * 4) + align_up((size_t)B * Hkv * 4);
 }
 
+template <int D, bool PAGED>
+hipError_t launch_sets(const VerifyArgs& p, hipStream_t s) {
+  // one 32-row query set when the packed rows fit, two otherwise
+  return (p.H / p.Hkv) * p.kq <= 32 ? launch<D, PAGED, 1>(p, s) : launch<D, PAGED, 2>(p, s);
+}
+
 hipError_t launch_verify_bf16(const VerifyArgs& p, hipStream_t s) {
-  if (p.paged) return p.d == 128 ? launch<128, true>(p, s) : launch<64, true>(p, s);
-  return p.d == 128 ? launch<128, false>(p, s) : launch<64, false>(p, s);
+  if (p.paged) return p.d == 128 ? launch_sets<128, true>(p, s) : launch_sets<64, true>(p, s);
+  return p.d == 128 ? launch_sets<128, false>(p, s) : launch_sets<64, false>(p, s);
 }
 
 }  // namespace attn

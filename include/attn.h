@@ -108,8 +108,9 @@ size_t attn_verify_workspace_bytes(int B, int H, int Hkv, int kq, int d);
  * with max_seqlen_k >= every seqlens_k[b] and max_seqlen_k <= cache_stride;
  * device values above it are clamped to it, negative values to 0.  Rows with
  * no visible key get O = 0 and lse = -inf.  dtype must be ATTN_BF16;
- * d in {64, 128}; (H / Hkv) * kq <= 32 (the query rows that share one KV head
- * are packed into one 32-row matrix tile).
+ * d in {64, 128}; (H / Hkv) * kq <= 64, else ATTN_ERR_UNSUPPORTED (the query
+ * rows that share one KV head are packed into one or two 32-row matrix
+ * tiles, so each cache byte is read once).
  */
 int attn_verify(const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* seqlens_k, int max_seqlen_k, int cache_stride,
@@ -128,8 +129,8 @@ int attn_verify(const void* q, const void* k_cache, const void* v_cache,
  * tree_mask[b][i] = 2^(i+1) - 1, for which the result equals attn_verify's
  * bit for bit.  A row that sees no key gets O = 0, lse = -inf.
  *
- *   tree_mask   [B, kq] uint32 (device); kq <= 32 follows from the packing
- *               limit (H / Hkv) * kq <= 32
+ *   tree_mask   [B, kq] uint32 (device); kq <= 32 (ATTN_ERR_UNSUPPORTED
+ *               above), besides the packing limit (H / Hkv) * kq <= 64
  *
  * All other arguments, the workspace and the errors are those of
  * attn_verify, plus ATTN_ERR_INVALID_ARG for a null or misaligned tree_mask
@@ -155,10 +156,12 @@ int attn_verify_tree(const void* q, const void* k_cache, const void* v_cache,
  *                     of sequence b (its keys i*page_size .. +page_size-1) is
  *                     physical page block_table[b][i].  Pages may be shared
  *                     between sequences (prefix sharing).  Only the entries
- *                     covering seqlens_k[b] keys are read; an entry outside
- *                     [0, num_pages) reads as zero keys and values.
- *   page_size         keys per page: a power of two in [32, 4096] (a multiple
- *                     of the kernel's 32-key step, so each step reads one
+ *                     covering seqlens_k[b] keys are read.  An entry outside
+ *                     [0, num_pages) maps its block to no storage: its keys
+ *                     do not exist and no query attends to them (a row left
+ *                     with no key gets O = 0 and lse = -inf).
+ *   page_size         keys per page: a power of two in [16, 4096] (each
+ *                     16-key half of the kernel's 32-key step reads one
  *                     page)
  *   max_seqlen_k      host bound, <= max_blocks_per_seq * page_size
  *

@@ -113,8 +113,9 @@ def call_verify(**kw):
     (dict(scale=0.0), bd.ATTN_ERR_INVALID_ARG),
     (dict(dtype=bd.ATTN_F32), bd.ATTN_ERR_UNSUPPORTED),
     (dict(d=80), bd.ATTN_ERR_UNSUPPORTED),
-    (dict(kq=9), bd.ATTN_ERR_UNSUPPORTED),        # 4 heads * 9 tokens > 32 packed rows
-    (dict(H=64, Hkv=1, kq=1), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(kq=17), bd.ATTN_ERR_UNSUPPORTED),       # 4 heads * 17 tokens > 64 packed rows
+    (dict(H=65, Hkv=1, kq=1), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(H=8, Hkv=8, kq=65), bd.ATTN_ERR_UNSUPPORTED),
     (dict(wsb=100), bd.ATTN_ERR_WORKSPACE),
 ])
 def test_verify_rejects(kw, code):
@@ -158,7 +159,8 @@ def call_paged(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(table=None), bd.ATTN_ERR_INVALID_ARG),
     (dict(table=FAKE + 2), bd.ATTN_ERR_INVALID_ARG),
-    (dict(page=16), bd.ATTN_ERR_INVALID_ARG),       # below the 32-key step
+    (dict(page=8), bd.ATTN_ERR_INVALID_ARG),        # below the 16-key half step
+    (dict(page=0), bd.ATTN_ERR_INVALID_ARG),
     (dict(page=48), bd.ATTN_ERR_INVALID_ARG),       # not a power of two
     (dict(page=8192), bd.ATTN_ERR_INVALID_ARG),
     (dict(maxs=6401), bd.ATTN_ERR_INVALID_ARG),     # more keys than the table covers (100 * 64)
@@ -170,7 +172,8 @@ def call_paged(**kw):
     (dict(scale=float("nan")), bd.ATTN_ERR_INVALID_ARG),
     (dict(dtype=bd.ATTN_F32), bd.ATTN_ERR_UNSUPPORTED),
     (dict(d=96), bd.ATTN_ERR_UNSUPPORTED),
-    (dict(kq=9), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(kq=17), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(H=64, Hkv=1, kq=2), bd.ATTN_ERR_UNSUPPORTED),
     (dict(wsb=100), bd.ATTN_ERR_WORKSPACE),
 ])
 def test_verify_paged_rejects(kw, code):
@@ -189,6 +192,15 @@ def test_verify_tree_rejects_missing_mask():
             a["stream"])
     assert bd.attn_verify_tree(*args, None, *tail) == bd.ATTN_ERR_INVALID_ARG
     assert bd.attn_verify_tree(*args, FAKE + 2, *tail) == bd.ATTN_ERR_INVALID_ARG
+    # 32-bit masks: at most 32 tree nodes, even where 64 packed rows would fit
+    a = verify_args(H=8, Hkv=8, kq=33)
+    tail = (a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["kq"], a["d"], a["scale"], a["dtype"], a["ws"], a["wsb"],
+            a["stream"])
+    assert bd.attn_verify_tree(*args, FAKE, *tail) == bd.ATTN_ERR_UNSUPPORTED
+    a = verify_args(H=8, Hkv=4, kq=33)  # 66 packed rows
+    tail = (a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["kq"], a["d"], a["scale"], a["dtype"], a["ws"], a["wsb"],
+            a["stream"])
+    assert bd.attn_verify_tree(*args, FAKE, *tail) == bd.ATTN_ERR_UNSUPPORTED
     a0 = verify_args(B=0, q=None, o=None, sl=None, k=None, v=None, ws=None, maxs=0, stride=0)
     assert bd.attn_verify_tree(a0["q"], a0["k"], a0["v"], a0["sl"], 0, 0, None, a0["o"], a0["lse"], 0, a0["H"],
                                a0["Hkv"], a0["kq"], a0["d"], a0["scale"], a0["dtype"], None, a0["wsb"],

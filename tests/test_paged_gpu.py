@@ -90,10 +90,17 @@ def paged_case(seed, lengths, H, Hkv, kq, d, page, shared=0, what=""):
     return check_paged(q, kp, vp, table, sl, page, o, lse, scale, what)
 
 
-@pytest.mark.parametrize("page", [32, 64, 256])
+@pytest.mark.parametrize("page", [16, 32, 64, 256])
 @pytest.mark.parametrize("d", [64, 128])
 def test_paged_matches_oracle(page, d):
     paged_case(page + d, [1000, 37, 5, 2500, 64, 33], 16, 4, 5, d, page, what="ragged")
+
+
+@pytest.mark.parametrize("page", [16, 64])
+@pytest.mark.parametrize("H,Hkv,kq", [(64, 8, 8), (32, 4, 6), (8, 8, 64)])
+def test_paged_two_query_tiles(page, H, Hkv, kq):
+    """More than 32 packed rows per KV head, through the block table."""
+    paged_case(page + H + kq, [1500, kq, 333, 2049], H, Hkv, kq, 128, page, what="paged-two-tiles")
 
 
 @pytest.mark.parametrize("page", [32, 128])
@@ -106,24 +113,37 @@ def test_paged_short_and_empty():
     paged_case(3, [0, 1, 4, 5, 6, 31, 32, 33], 8, 2, 5, 128, 32, what="short")
 
 
-def test_paged_invalid_entries_read_zero():
-    """Table entries outside [0, num_pages) read as zero keys and values."""
-    rng = np.random.default_rng(5)
-    B, H, Hkv, kq, d, page = 2, 8, 2, 5, 128, 64
-    sl = np.array([300, 200], dtype=np.int32)
+@pytest.mark.parametrize("page", [16, 64])
+def test_paged_invalid_entries_are_absent(page):
+    """Table entries outside [0, num_pages) map their block to no storage:
+    those keys do not exist and no query attends to them ("Warmup Guide",
+    Ch.8: the block table is the only map from logical to physical blocks).
+    Sequence 0 loses a middle block, sequence 1 its first block, sequence 2
+    the block holding its new tokens (its rows see only older keys), and
+    sequence 3 every block (its rows see nothing: O = 0, LSE = -inf)."""
+    rng = np.random.default_rng(5 + page)
+    B, H, Hkv, kq, d = 4, 8, 2, 5, 128
+    sl = np.array([300, 200, 4 * page + 3, 2 * page], dtype=np.int32)
+    smax = int(sl.max())
     q = synth.normal(rng, (B, H, kq, d), "bf16").cuda()
-    k = synth.normal(rng, (B, Hkv, 300, d), "bf16").cuda()
-    v = synth.normal(rng, (B, Hkv, 300, d), "bf16").cuda()
+    k = synth.normal(rng, (B, Hkv, smax, d), "bf16").cuda()
+    v = synth.normal(rng, (B, Hkv, smax, d), "bf16").cuda()
     kp, vp, table = to_pages(k, v, sl, page, rng, spare=0)
+    npg = kp.shape[0]
     table[0, 1] = -1
-    table[1, 0] = kp.shape[0] + 10
+    table[1, 0] = npg + 10
+    table[2, (sl[2] - 1) // page] = -7
+    table[2, (sl[2] - kq) // page] = -7
+    table[3, :2] = [-1, npg]
     scale = float(np.float32(d ** -0.5))
-    P.log(f"[paged] invalid entries table={table.tolist()}")
+    P.log(f"[paged] invalid entries page={page} table={table.tolist()}")
     o, lse = run_paged(q, kp, vp, table, sl, scale)
     check_paged(q, kp, vp, table, sl, page, o, lse, scale, "invalid-entries")
+    assert torch.all(o[3] == 0) and torch.all(torch.isneginf(lse[3]))
+    assert torch.all(torch.isfinite(lse[:3]))
 
 
-@pytest.mark.parametrize("page", [64, 1024])
+@pytest.mark.parametrize("page", [16, 64, 1024])
 def test_paged_full_workload_bitwise_equals_contiguous(page):
     """Seed-4 verify workload: the paged call over randomly permuted pages gives
     bit-identical O and LSE to the contiguous call (same logical cache, same

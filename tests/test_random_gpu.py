@@ -21,17 +21,19 @@ pytestmark = pytest.mark.gpu
 N = 12  # cases per entry point
 
 
-def heads(rng, kq=1, cap=32):
+def heads(rng, kq=1, cap=64):
     """(H, Hkv) with (H / Hkv) * kq <= cap."""
     Hkv = int(rng.choice([1, 2, 4]))
     G = int(rng.choice([g for g in (1, 2, 4, 8) if g * kq <= cap]))
+    if G * kq > 32:
+        P.log(f"    ({G * kq} packed rows: two query tiles)")
     return Hkv * G, Hkv
 
 
 @pytest.mark.parametrize("i", range(N))
 def test_random_fwd(i):
     rng = np.random.default_rng(100 + i)
-    H, Hkv = heads(rng)
+    H, Hkv = heads(rng, cap=8)
     B, d = int(rng.integers(1, 3)), int(rng.choice([64, 128]))
     Sq = int(rng.integers(1, 700))
     Sk = Sq if rng.random() < 0.4 else int(rng.integers(1, 700))
@@ -69,7 +71,7 @@ def test_random_paged(i):
     kq = int(rng.integers(1, 9))
     H, Hkv = heads(rng, kq)
     B, d = int(rng.integers(1, 4)), int(rng.choice([64, 128]))
-    page = int(rng.choice([32, 64, 128, 256, 1024]))
+    page = int(rng.choice([16, 32, 64, 128, 256, 1024]))
     lengths = [int(x) for x in rng.integers(0, 3000, B)]
     shared = int(rng.integers(0, 3)) if B > 1 and min(lengths) > 3 * page else 0
     TP.paged_case(4000 + i, lengths, H, Hkv, kq, d, page, shared=shared, what=f"random{i}")
@@ -85,7 +87,7 @@ def test_random_spec_accept(i):
 @pytest.mark.parametrize("i", range(N))
 def test_random_bwd(i):
     rng = np.random.default_rng(600 + i)
-    H, Hkv = heads(rng)
+    H, Hkv = heads(rng, cap=8)
     H = min(H, 8)
     Hkv = Hkv if H % Hkv == 0 else 1
     B, d = int(rng.integers(1, 3)), int(rng.choice([64, 128]))

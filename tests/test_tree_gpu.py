@@ -74,7 +74,8 @@ def tree_case(seed, lengths, H, Hkv, kq, d, masks=None, what=""):
     return q, k, v, sl, o, lse
 
 
-@pytest.mark.parametrize("H,Hkv,kq", [(32, 8, 5), (32, 8, 8), (8, 8, 16), (8, 8, 32), (16, 1, 2)])
+@pytest.mark.parametrize("H,Hkv,kq", [(32, 8, 5), (32, 8, 8), (8, 8, 16), (8, 8, 32), (16, 1, 2),
+                                      (32, 8, 16), (16, 8, 32), (64, 8, 8), (8, 1, 7)])
 @pytest.mark.parametrize("d", [64, 128])
 def test_random_trees(H, Hkv, kq, d):
     tree_case(kq * 7 + d, [3000, 40, kq, 1025, 700], H, Hkv, kq, d, what="random-trees")

@@ -83,6 +83,25 @@ def test_gqa_packing(H, Hkv, kq):
     verify_case(H + Hkv + kq, [700, 3000, 5], H, Hkv, kq, 128, what="gqa")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("H,Hkv,kq", [(32, 4, 5), (32, 4, 8), (64, 8, 6), (16, 1, 4), (8, 8, 64), (4, 2, 32),
+                                      (64, 1, 1), (24, 3, 7)])
+def test_two_query_tiles(H, Hkv, kq, d):
+    """(H/Hkv)*kq between 33 and 64: the rows that share a KV head fill two
+    32-row tiles, both fed from the same K/V operands (a GQA-8 model
+    verifying up to 8 drafts, a 64-token chain on one KV head, ...)."""
+    verify_case(H * 3 + Hkv + kq + d, [2500, 40, kq, 1025, 700 + kq], H, Hkv, kq, d, what="two-tiles")
+
+
+@pytest.mark.parametrize("kq", [5, 8])
+def test_gqa8_on_workload_lengths(kq):
+    """GQA-8 (64 query heads over the 8 KV heads) with the verify workload's
+    cache lengths: 8*kq packed rows per KV head."""
+    w = synth.VERIFY_BF16
+    L = synth.verify_lengths(w)
+    verify_case(800 + kq, [int(x) + kq for x in L], 64, 8, kq, 128, what=f"gqa8-kq{kq}")
+
+
 def test_head_dim_64():
     verify_case(64, [2500, 17, 1024], 16, 4, 5, 64, what="d64")
 

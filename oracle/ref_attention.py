@@ -192,7 +192,33 @@ def verify(q, k_cache, v_cache, seqlens_k, scale: float,
     return out, lse
 
 
-def attention_backward(q, k, v, dout, causal: bool, scale: float):
+def _bwd_kv_group(q, k, v, dout, vis, scale):
+    """Gradients for the query heads q/dout [G, Sq, d] that read one KV head
+    k/v [Sk, d]: dQ [G, Sq, d] and that KV head's dK, dV [Sk, d] (summed over
+    the G query heads in order)."""
+    G, Sq, _ = q.shape
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for h in range(G):
+        s = scale * (q[h] @ k.T)
+        s = np.where(vis, s, -np.inf)
+        P = np.zeros_like(s)
+        for i in range(Sq):
+            if vis[i].any():
+                m = np.max(s[i])
+                e = np.exp(s[i] - m)
+                P[i] = e / np.sum(e)
+        dv += P.T @ dout[h]
+        dP = dout[h] @ v.T
+        dS = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
+        dq[h] = scale * (dS @ k)
+        dk += scale * (dS.T @ q[h])
+    return dq, dk, dv
+
+
+def attention_backward(q, k, v, dout, causal: bool, scale: float,
+                       kv_heads: Optional[Sequence[Tuple[int, int]]] = None, workers: int = 1):
     """Gradients (dQ, dK, dV) of sum(dout * O) for O = attention(q, k, v).
 
     "Warmup Guide -- Inference Optimization at Depth", Ch.4 (backward pass):
@@ -205,6 +231,9 @@ def attention_backward(q, k, v, dout, causal: bool, scale: float):
         dQ = scale dS K;  dK = scale dS^T Q.
     For grouped-query attention dK and dV of a KV head sum over the query
     heads that read it.  Rows that see no key contribute nothing.
+    ``kv_heads`` restricts the work to those (b, KV head g) pairs and their
+    query heads (other gradients stay 0); ``workers`` > 1 runs the pairs on
+    that many threads, one BLAS thread each.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -217,22 +246,17 @@ def attention_backward(q, k, v, dout, causal: bool, scale: float):
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    for b in range(B):
-        for h in range(H):
-            g = h // G
-            s = scale * (q[b, h] @ k[b, g].T)
-            s = np.where(vis, s, -np.inf)
-            P = np.zeros_like(s)
-            for i in range(Sq):
-                if vis[i].any():
-                    m = np.max(s[i])
-                    e = np.exp(s[i] - m)
-                    P[i] = e / np.sum(e)
-            dv[b, g] += P.T @ dout[b, h]
-            dP = dout[b, h] @ v[b, g].T
-            dS = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
-            dq[b, h] = scale * (dS @ k[b, g])
-            dk[b, g] += scale * (dS.T @ q[b, h])
+    todo = [(b, g) for b in range(B) for g in range(Hkv)] if kv_heads is None else list(kv_heads)
+    tasks = [(q[b, g * G:(g + 1) * G], k[b, g], v[b, g], dout[b, g * G:(g + 1) * G], vis, scale) for b, g in todo]
+    if workers > 1 and len(tasks) > 1:
+        with _blas_one_thread(), ThreadPoolExecutor(max_workers=workers) as ex:
+            results = list(ex.map(lambda t: _bwd_kv_group(*t), tasks))
+    else:
+        results = [_bwd_kv_group(*t) for t in tasks]
+    for (b, g), (dq_g, dk_g, dv_g) in zip(todo, results):
+        dq[b, g * G:(g + 1) * G] = dq_g
+        dk[b, g] = dk_g
+        dv[b, g] = dv_g
     return dq, dk, dv
 
 

@@ -3,7 +3,7 @@
 Argument marshalling only: torch tensors supply device memory and the current
 stream, every step of the computation runs in the library's HIP kernels.  The
 raw entry points keep the C names (``attn_fwd``, ``attn_verify``,
-``attn_verify_tree``, ``attn_verify_paged``, ``attn_verify_workspace_bytes``,
+``attn_verify_noalloc``, ``attn_verify_tree``, ``attn_verify_paged``, ``attn_verify_workspace_bytes``,
 ``attn_spec_accept``, ``attn_spec_accept_workspace_bytes``, ``attn_bwd``,
 ``attn_bwd_workspace_bytes``, ``attn_strerror``); ``fwd``, ``bwd``,
 ``verify``, ``verify_tree``, ``verify_paged`` and ``spec_accept`` are
@@ -29,6 +29,7 @@ ATTN_ERR_INVALID_ARG = -1
 ATTN_ERR_UNSUPPORTED = -2
 ATTN_ERR_WORKSPACE = -3
 ATTN_ERR_HIP = -4
+ATTN_ERR_TOO_LARGE = -5
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m exact_attention_04_amd.build`")
@@ -43,6 +44,8 @@ lib.attn_verify_workspace_bytes.restype = _sz
 lib.attn_verify_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]  # B, H, Hkv, kq, d
 lib.attn_verify.restype = _i
 lib.attn_verify.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]
+lib.attn_verify_noalloc.restype = _i
+lib.attn_verify_noalloc.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]
 lib.attn_verify_tree.restype = _i
 lib.attn_verify_tree.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz,
                                  _vp]
@@ -60,8 +63,8 @@ lib.attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i
 lib.attn_strerror.restype = ctypes.c_char_p
 lib.attn_strerror.argtypes = [_i]
 
-EXPORTED = ("attn_fwd", "attn_verify", "attn_verify_tree", "attn_verify_paged", "attn_verify_workspace_bytes",
-            "attn_spec_accept", "attn_spec_accept_workspace_bytes", "attn_bwd", "attn_bwd_workspace_bytes",
+EXPORTED = ("attn_fwd", "attn_verify", "attn_verify_noalloc", "attn_verify_tree", "attn_verify_paged",
+            "attn_verify_workspace_bytes", "attn_spec_accept", "attn_spec_accept_workspace_bytes", "attn_bwd", "attn_bwd_workspace_bytes",
             "attn_strerror")
 
 
@@ -89,6 +92,13 @@ def attn_verify(q, k_cache, v_cache, seqlens_k, max_seqlen_k, cache_stride, o, l
     """Raw C entry point (device pointers as ints); returns the ATTN_* code."""
     return lib.attn_verify(q, k_cache, v_cache, seqlens_k, max_seqlen_k, cache_stride, o, lse, B, H, Hkv,
                            kq, d, float(scale), dtype, workspace, workspace_bytes, stream)
+
+
+def attn_verify_noalloc(q, k_cache, v_cache, seqlens_k, max_seqlen_k, cache_stride, o, lse, B, H, Hkv, kq, d,
+                        scale, dtype, stream) -> int:
+    """Raw C entry point (device pointers as ints); returns the ATTN_* code."""
+    return lib.attn_verify_noalloc(q, k_cache, v_cache, seqlens_k, max_seqlen_k, cache_stride, o, lse, B, H, Hkv,
+                                   kq, d, float(scale), dtype, stream)
 
 
 def attn_verify_tree(q, k_cache, v_cache, seqlens_k, max_seqlen_k, cache_stride, tree_mask, o, lse, B, H, Hkv,

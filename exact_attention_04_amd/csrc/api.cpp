@@ -69,7 +69,7 @@ namespace {
 int verify_contiguous(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens_k,
                       int max_seqlen_k, int cache_stride, const uint32_t* tree_mask, bool tree, void* o,
                       float* lse, int B, int H, int Hkv, int kq, int d, float scale, int dtype,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+                      void* workspace, size_t workspace_bytes, void* stream, bool noalloc = false) {
   if (B < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || kq < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
   if (max_seqlen_k < 0 || cache_stride < 0 || max_seqlen_k > cache_stride) return ATTN_ERR_INVALID_ARG;
   if (!scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
@@ -87,8 +87,12 @@ int verify_contiguous(const void* q, const void* k_cache, const void* v_cache, c
   if (tree && B > 0 && (tree_mask == nullptr || !aligned4(tree_mask))) return ATTN_ERR_INVALID_ARG;
   if (lse != nullptr && !aligned4(lse)) return ATTN_ERR_INVALID_ARG;
   const size_t need = attn::verify_workspace_bytes(B, H, Hkv, kq, d);
-  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-  if (need > 0 && (workspace == nullptr || !aligned16(workspace))) return ATTN_ERR_INVALID_ARG;
+  if (noalloc) {
+    if (need > attn::verify_noalloc_scratch_bytes()) return ATTN_ERR_TOO_LARGE;
+  } else {
+    if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (need > 0 && (workspace == nullptr || !aligned16(workspace))) return ATTN_ERR_INVALID_ARG;
+  }
   if (nq == 0) return ATTN_OK;
 
   attn::VerifyArgs a;
@@ -113,7 +117,8 @@ int verify_contiguous(const void* q, const void* k_cache, const void* v_cache, c
   a.cache_stride = cache_stride;
   a.scale = scale;
   a.workspace = workspace;
-  const hipError_t e = attn::launch_verify_bf16(a, static_cast<hipStream_t>(stream));
+  const hipError_t e = noalloc ? attn::launch_verify_bf16_noalloc(a, static_cast<hipStream_t>(stream))
+                               : attn::launch_verify_bf16(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -126,6 +131,14 @@ extern "C" int attn_verify(const void* q, const void* k_cache, const void* v_cac
                            void* stream) {
   return verify_contiguous(q, k_cache, v_cache, seqlens_k, max_seqlen_k, cache_stride, nullptr, false, o, lse,
                            B, H, Hkv, kq, d, scale, dtype, workspace, workspace_bytes, stream);
+}
+
+extern "C" int attn_verify_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* seqlens_k, int max_seqlen_k, int cache_stride,
+                                   void* o, float* lse, int B, int H, int Hkv, int kq, int d,
+                                   float scale, int dtype, void* stream) {
+  return verify_contiguous(q, k_cache, v_cache, seqlens_k, max_seqlen_k, cache_stride, nullptr, false, o, lse,
+                           B, H, Hkv, kq, d, scale, dtype, nullptr, 0, stream, true);
 }
 
 extern "C" int attn_verify_tree(const void* q, const void* k_cache, const void* v_cache,
@@ -288,6 +301,7 @@ extern "C" const char* attn_strerror(int code) {
     case ATTN_ERR_UNSUPPORTED: return "unsupported configuration (head dim, dtype, or query packing)";
     case ATTN_ERR_WORKSPACE: return "workspace too small";
     case ATTN_ERR_HIP: return "HIP kernel launch failed";
+    case ATTN_ERR_TOO_LARGE: return "sizes need more than the static scratch of attn_verify_noalloc (32 MiB)";
     default: return "unknown error code";
   }
 }

@@ -67,6 +67,10 @@ struct BwdArgs {
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_verify_bf16(const VerifyArgs& a, hipStream_t s);
+// attn_verify with the library's static per-device scratch as the workspace
+// (a.workspace is ignored); sizes must fit verify_noalloc_scratch_bytes().
+hipError_t launch_verify_bf16_noalloc(const VerifyArgs& a, hipStream_t s);
+size_t verify_noalloc_scratch_bytes();
 hipError_t launch_spec_accept(const SpecAcceptArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
 

@@ -43,6 +43,9 @@
 // Merge kernel -- one wave per output row combines its segment's piece
 // partials (weights exp(LSE_p - LSE)) and writes O (bf16) and LSE (natural
 // log).
+#include <atomic>
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -661,7 +664,51 @@ hipError_t launch(const VerifyArgs& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---- the allocation-free variant.  Its partials live in a file-scope
+// device array instead of a caller workspace.  Each GPU the library runs on
+// holds its own copy (at its own address) until the process ends; in host
+// code the array's name is not a device address, so its address on the
+// current device is looked up once per device with hipGetSymbolAddress and
+// only that pointer is ever handed to kernels.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // on the current device
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 }  // namespace
+
+size_t verify_noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+hipError_t launch_verify_bf16_noalloc(const VerifyArgs& p, hipStream_t s) {
+  // The split kernel writes every partial slot and piece count the merge
+  // reads in the same call, so the scratch needs no clearing between calls.
+  VerifyArgs a = p;
+  hipError_t e = scratch_address(&a.workspace);
+  if (e != hipSuccess) return e;
+  return launch_verify_bf16(a, s);
+}
 
 int verify_split_workgroups() { return kSplitWgs; }
 

@@ -34,6 +34,7 @@ extern "C" {
 #define ATTN_ERR_UNSUPPORTED (-2) /* head dim not 64/128, dtype, verify query packing */
 #define ATTN_ERR_WORKSPACE (-3)   /* verify workspace smaller than required */
 #define ATTN_ERR_HIP (-4)         /* the kernel launch failed */
+#define ATTN_ERR_TOO_LARGE (-5)   /* attn_verify_noalloc: sizes beyond its static scratch */
 
 /*
  * attn_fwd -- O = softmax(scale * Q K^T + mask) V, and per-row LSE.
@@ -117,6 +118,29 @@ int attn_verify(const void* q, const void* k_cache, const void* v_cache,
                 void* o, float* lse, int B, int H, int Hkv, int kq, int d,
                 float scale, int dtype, void* workspace, size_t workspace_bytes,
                 void* stream);
+
+/*
+ * attn_verify_noalloc -- attn_verify without a workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments (minus the
+ * workspace), kernels, semantics and bitwise results as attn_verify.  The
+ * partials live in a static device array of 32 MiB that each GPU holds from
+ * the library's load until the process ends; its address on the current
+ * device is looked up on the first call on that device.  The stream must
+ * belong to the current device.  Sizes whose
+ * attn_verify_workspace_bytes(B, H, Hkv, kq, d) exceed 32 MiB are rejected
+ * with ATTN_ERR_TOO_LARGE before any HIP call (the verify workload of 8
+ * sequences, 32 query heads over 8 KV heads, kq = 5, d = 128 needs 22.5 MB).
+ * The call allocates and frees nothing.  Every call on one GPU shares that
+ * GPU's array and overwrites it: calls that overlap on one device (on
+ * different streams, or from different host threads without ordering) race
+ * and give wrong results; order them.  Nothing needs clearing between calls
+ * (each call writes every slot it reads).
+ */
+int attn_verify_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* seqlens_k, int max_seqlen_k, int cache_stride,
+                        void* o, float* lse, int B, int H, int Hkv, int kq, int d,
+                        float scale, int dtype, void* stream);
 
 /*
  * attn_verify_tree -- attn_verify for a draft *tree* instead of a chain

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_error_strings():
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert bd.attn_strerror(code) and "unknown" not in bd.attn_strerror(code)
     assert "unknown" in bd.attn_strerror(7)
 
@@ -137,6 +137,35 @@ def test_verify_workspace_formula():
 
 def test_verify_empty_batch_is_a_noop():
     assert call_verify(B=0, q=None, o=None, sl=None, k=None, v=None, ws=None, maxs=0, stride=0) == bd.ATTN_OK
+
+
+def call_noalloc(**kw):
+    a = verify_args(**kw)
+    return bd.attn_verify_noalloc(a["q"], a["k"], a["v"], a["sl"], a["maxs"], a["stride"], a["o"], a["lse"], a["B"],
+                                  a["H"], a["Hkv"], a["kq"], a["d"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), bd.ATTN_ERR_INVALID_ARG),
+    (dict(sl=FAKE + 2), bd.ATTN_ERR_INVALID_ARG),
+    (dict(maxs=3001), bd.ATTN_ERR_INVALID_ARG),
+    (dict(kq=0), bd.ATTN_ERR_INVALID_ARG),
+    (dict(dtype=bd.ATTN_F32), bd.ATTN_ERR_UNSUPPORTED),
+    (dict(kq=17), bd.ATTN_ERR_UNSUPPORTED),
+    # partials beyond the 32 MiB static scratch (B=12 at the verify workload's
+    # other sizes needs 33.7 MB; B=11 fits)
+    (dict(B=12), bd.ATTN_ERR_TOO_LARGE),
+    (dict(B=64, kq=8), bd.ATTN_ERR_TOO_LARGE),
+])
+def test_verify_noalloc_rejects(kw, code):
+    """Argument checks and the static-scratch limit, all on the host before any HIP call."""
+    assert call_noalloc(**kw) == code
+
+
+def test_verify_noalloc_limit_matches_the_workspace_formula():
+    lim = 32 << 20
+    assert bd.attn_verify_workspace_bytes(11, 32, 8, 5, 128) <= lim < bd.attn_verify_workspace_bytes(12, 32, 8, 5, 128)
+    assert call_noalloc(B=0, q=None, o=None, sl=None, k=None, v=None, maxs=0, stride=0) == bd.ATTN_OK
 
 
 def paged_args(**kw):

@@ -8,7 +8,13 @@ generator (:mod:`exact_attention_04_amd.synth`) can be used without the
 library; every compute entry point raises if the library is missing.
 """
 
-__all__ = ["attn_fwd", "attn_verify", "attn_verify_workspace_bytes", "fwd", "verify"]
+# the C entry points (raw, device pointers as ints) and the tensor-level calls
+__all__ = [
+    "attn_fwd", "attn_verify", "attn_verify_noalloc", "attn_verify_tree", "attn_verify_paged",
+    "attn_verify_workspace_bytes", "attn_spec_accept", "attn_spec_accept_workspace_bytes", "attn_bwd",
+    "attn_bwd_workspace_bytes", "attn_strerror",
+    "fwd", "bwd", "verify", "verify_tree", "verify_paged", "spec_accept",
+]
 
 
 def __getattr__(name):

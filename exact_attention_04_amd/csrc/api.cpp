@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "../../include/attn.h"
 #include "launch.h"
 
@@ -19,6 +21,20 @@ bool ptr_ok(const void* p, size_t elems) { return elems == 0 || (p != nullptr &&
 bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
 
 constexpr size_t kMaxElems = (size_t)1 << 40;  // keeps every index product in 64-bit range
+constexpr int kMaxSeq = 1 << 30;               // query/key counts: row indices plus a block fit int32
+
+// Product of non-negative sizes, exact or saturated at SIZE_MAX: it never
+// wraps, so an oversized request cannot pass a limit check.  Any zero factor
+// gives 0.
+size_t prod(std::initializer_list<long long> xs) {
+  size_t p = 1;
+  bool over = false;
+  for (long long x : xs) {
+    if (x == 0) return 0;
+    over |= __builtin_mul_overflow(p, (size_t)x, &p);
+  }
+  return over ? SIZE_MAX : p;
+}
 
 }  // namespace
 
@@ -29,13 +45,15 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   if (!scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  const size_t nq = (size_t)B * H * Sq * d;
-  const size_t nk = (size_t)B * Hkv * Sk * d;
+  if (Sq > kMaxSeq || Sk > kMaxSeq) return ATTN_ERR_UNSUPPORTED;
+  const size_t nq = prod({B, H, Sq, d});
+  const size_t nk = prod({B, Hkv, Sk, d});
   if (nq > kMaxElems || nk > kMaxElems) return ATTN_ERR_INVALID_ARG;
   // one workgroup per (batch, head, query block) must fit the grid: blocks
   // of 256 rows (bf16) or 16 rows (fp32)
-  const size_t rows_per_block = dtype == ATTN_F32 ? 16 : 256;
-  if ((size_t)B * H * (((size_t)Sq + rows_per_block - 1) / rows_per_block) > 0x7fffffffu) return ATTN_ERR_INVALID_ARG;
+  const long long rows_per_block = dtype == ATTN_F32 ? 16 : 256;
+  if (prod({B, H, ((long long)Sq + rows_per_block - 1) / rows_per_block}) > 0x7fffffffu)
+    return ATTN_ERR_INVALID_ARG;
   if (!ptr_ok(q, nq) || !ptr_ok(o, nq) || !ptr_ok(k, nk) || !ptr_ok(v, nk)) return ATTN_ERR_INVALID_ARG;
   if (lse != nullptr && !aligned4(lse)) return ATTN_ERR_INVALID_ARG;
   if (nq == 0) return ATTN_OK;
@@ -61,6 +79,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
 
 extern "C" size_t attn_verify_workspace_bytes(int B, int H, int Hkv, int kq, int d) {
   if (B < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || kq < 1 || (d != 64 && d != 128)) return 0;
+  if (prod({B, H, kq, d}) > kMaxElems) return 0;  // larger than any call accepts
   return attn::verify_workspace_bytes(B, H, Hkv, kq, d);
 }
 
@@ -78,8 +97,8 @@ int verify_contiguous(const void* q, const void* k_cache, const void* v_cache, c
   if ((long long)(H / Hkv) * kq > 64) return ATTN_ERR_UNSUPPORTED;  // two 32-row query tiles at most
   if (tree && kq > 32) return ATTN_ERR_UNSUPPORTED;                  // 32-bit visibility masks
   if ((long long)B * max_seqlen_k >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;  // total keys fit int32
-  const size_t nq = (size_t)B * H * kq * d;
-  const size_t nk = (size_t)B * Hkv * cache_stride * d;
+  const size_t nq = prod({B, H, kq, d});
+  const size_t nk = prod({B, Hkv, cache_stride, d});
   if (nq > kMaxElems || nk > kMaxElems) return ATTN_ERR_INVALID_ARG;
   if (!ptr_ok(q, nq) || !ptr_ok(o, nq) || !ptr_ok(k_cache, nk) || !ptr_ok(v_cache, nk))
     return ATTN_ERR_INVALID_ARG;
@@ -167,9 +186,9 @@ extern "C" int attn_verify_paged(const void* q, const void* k_pages, const void*
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   if ((long long)(H / Hkv) * kq > 64) return ATTN_ERR_UNSUPPORTED;  // two 32-row query tiles at most
   if ((long long)B * max_seqlen_k >= (1LL << 31)) return ATTN_ERR_UNSUPPORTED;  // total keys fit int32
-  const size_t nq = (size_t)B * H * kq * d;
-  const size_t nk = (size_t)num_pages * Hkv * page_size * d;
-  const size_t nt = (size_t)B * max_blocks_per_seq;
+  const size_t nq = prod({B, H, kq, d});
+  const size_t nk = prod({num_pages, Hkv, page_size, d});
+  const size_t nt = prod({B, max_blocks_per_seq});
   if (nq > kMaxElems || nk > kMaxElems || nt > kMaxElems) return ATTN_ERR_INVALID_ARG;
   if (!ptr_ok(q, nq) || !ptr_ok(o, nq) || !ptr_ok(k_pages, nk) || !ptr_ok(v_pages, nk))
     return ATTN_ERR_INVALID_ARG;
@@ -219,9 +238,9 @@ extern "C" int attn_spec_accept(const int32_t* draft_tokens, const float* draft_
                                 void* stream) {
   if (B < 0 || k < 0 || V < 1) return ATTN_ERR_INVALID_ARG;
   if (V > (1 << 22)) return ATTN_ERR_UNSUPPORTED;  // fixed-point sums stay below 2^62
-  if ((size_t)B * (k + 1) * V > kMaxElems) return ATTN_ERR_INVALID_ARG;
+  if (prod({B, (long long)k + 1, V}) > kMaxElems) return ATTN_ERR_INVALID_ARG;
   if (B == 0) return ATTN_OK;
-  const size_t nq = (size_t)B * k * V;
+  const size_t nq = prod({B, k, V});
   if (k > 0 && (draft_tokens == nullptr || !aligned4(draft_tokens) || u_accept == nullptr ||
                 !aligned4(u_accept) || nq == 0 || draft_probs == nullptr || !aligned4(draft_probs)))
     return ATTN_ERR_INVALID_ARG;
@@ -249,6 +268,7 @@ extern "C" int attn_spec_accept(const int32_t* draft_tokens, const float* draft_
 
 extern "C" size_t attn_bwd_workspace_bytes(int B, int H, int Sq) {
   if (B < 0 || H < 1 || Sq < 0) return 0;
+  if (prod({B, H, Sq}) > kMaxElems) return 0;  // larger than any call accepts
   return attn::bwd_workspace_bytes(B, H, Sq);
 }
 
@@ -260,10 +280,11 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   if (!scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  const size_t nq = (size_t)B * H * Sq * d;
-  const size_t nk = (size_t)B * Hkv * Sk * d;
+  if (Sq > kMaxSeq || Sk > kMaxSeq) return ATTN_ERR_UNSUPPORTED;
+  const size_t nq = prod({B, H, Sq, d});
+  const size_t nk = prod({B, Hkv, Sk, d});
   if (nq > kMaxElems || nk > kMaxElems) return ATTN_ERR_INVALID_ARG;
-  if ((size_t)B * H * (size_t)((Sq + 127) / 128) > 0x7fffffffu) return ATTN_ERR_INVALID_ARG;
+  if (prod({B, H, ((long long)Sq + 127) / 128}) > 0x7fffffffu) return ATTN_ERR_INVALID_ARG;
   if (!ptr_ok(q, nq) || !ptr_ok(o, nq) || !ptr_ok(dout, nq) || !ptr_ok(dq, nq)) return ATTN_ERR_INVALID_ARG;
   if (!ptr_ok(k, nk) || !ptr_ok(v, nk) || !ptr_ok(dk, nk) || !ptr_ok(dv, nk)) return ATTN_ERR_INVALID_ARG;
   if (nq > 0 && (lse == nullptr || !aligned4(lse))) return ATTN_ERR_INVALID_ARG;

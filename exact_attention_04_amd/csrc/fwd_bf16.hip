@@ -11,8 +11,8 @@
 // Mapping onto CDNA4:
 //   * one workgroup = 8 waves = 256 query rows of one (batch, head), 32 rows
 //     per wave; K/V tiles of 64 keys are shared by all eight waves through
-//     LDS, two (or three) buffers each, filled by direct HBM->LDS loads
-//     (buffer_load ... lds) issued one (or two) tiles ahead, so no registers
+//     LDS, two buffers each, filled by direct HBM->LDS loads
+//     (buffer_load ... lds) issued one tile ahead, so no registers
 //     hold staged data;
 //   * every tile is handled in two phases per wave: a matrix phase (scores of
 //     the next tile, S_{j+1}^T = K_{j+1} Q^T, and this tile's output update,
@@ -50,30 +50,12 @@
 namespace attn {
 namespace {
 
-// Whether a wave raises its issue priority during its matrix phase, and
-// the number of LDS buffers per K/V tile stream (2 or 3).
-#ifndef ATTN_FWD_PRIO
-#define ATTN_FWD_PRIO 0
-#endif
-#ifndef ATTN_FWD_STAGES
-#define ATTN_FWD_STAGES 2
-#endif
-// Whether the sum of the bf16-rounded probabilities comes from the matrix
-// cores (an all-ones block appended to V^T) instead of v_dot2 on the VALU.
-#ifndef ATTN_FWD_MFMA_LSUM
-#define ATTN_FWD_MFMA_LSUM 0
-#endif
-// Matrix phase schedule: how many MFMAs ahead the LDS operand reads are
-// issued (0: leave it to the compiler), and whether the phase boundaries are
-// scheduling fences (PIN).
-#ifndef ATTN_FWD_KPRE
-#define ATTN_FWD_KPRE 4
-#endif
-#ifndef ATTN_FWD_PIN
-#define ATTN_FWD_PIN 1
-#endif
-constexpr int kStages = ATTN_FWD_STAGES;
-static_assert(kStages == 2 || kStages == 3, "two or three tile buffers");
+// Two LDS buffers per K/V tile stream; each LDS operand read of a matrix
+// phase is issued kReadAhead MFMAs before the MFMA that consumes it.  (A
+// third buffer, deeper read-ahead, wave priorities and matrix-core row sums
+// were each measured and gave nothing.)
+constexpr int kStages = 2;
+constexpr int kReadAhead = 4;
 constexpr int kWaves = 8;               // two groups of four, one wave of each per SIMD
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBr = 32 * kWaves;        // query rows per workgroup
@@ -101,15 +83,9 @@ struct FwdKernelArgs {
 // fence would wait for them too: they write LDS); where a tile must have
 // landed, vmcnt is waited for explicitly first.
 __device__ __forceinline__ void lds_barrier() {
-  if (ATTN_FWD_PIN) __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  if (ATTN_FWD_PIN) __builtin_amdgcn_sched_barrier(0);
-}
-__device__ __forceinline__ void prio_matrix() {
-  if (ATTN_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
-}
-__device__ __forceinline__ void prio_vector() {
-  if (ATTN_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Scheduling pipeline of a matrix phase: KM score MFMAs (one K read each)
@@ -143,17 +119,15 @@ fwd_bf16_kernel(FwdKernelArgs a) {
   constexpr int INSN_PER_WAVE = TILE * 2 / 1024 / kWaves;
   static_assert(INSN_PER_WAVE >= 1, "every wave loads part of each tile");
 
-  // kStages buffers each for K and V tiles, one LDS object per buffer, so
-  // the compiler can prove that loads into one buffer never alias reads of
+  // two buffers each for K and V tiles, one LDS object per buffer, so the
+  // compiler can prove that loads into one buffer never alias reads of
   // another
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t k_lds2[kStages > 2 ? TILE : 1];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds2[kStages > 2 ? TILE : 1];
-  auto kbuf = [&](const int I) __attribute__((always_inline)) { return I == 0 ? k_lds0 : I == 1 ? k_lds1 : k_lds2; };
-  auto vbuf = [&](const int I) __attribute__((always_inline)) { return I == 0 ? v_lds0 : I == 1 ? v_lds1 : v_lds2; };
+  auto kbuf = [&](const int I) __attribute__((always_inline)) { return I == 0 ? k_lds0 : k_lds1; };
+  auto vbuf = [&](const int I) __attribute__((always_inline)) { return I == 0 ? v_lds0 : v_lds1; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -244,7 +218,6 @@ fwd_bf16_kernel(FwdKernelArgs a) {
   float m_ref = -INFINITY;  // reference max, base-2 domain (scaled logits * log2 e)
   float l_run = 0.f;        // running denominator, this lane's keys only
   float l_rnd = 0.f;        // same, of the bf16-rounded probabilities
-  f32x16 acc_l = f32x16{};  // with the MFMA sum: every register holds l_rnd of the lane's query
 
   // Per-lane LDS byte offsets, fixed for the whole kernel (buffer and tile
   // offsets are immediates).  K A-operand of block kb, step ks: row
@@ -312,10 +285,6 @@ fwd_bf16_kernel(FwdKernelArgs a) {
     m_ref = raise ? mx : m_ref;
     l_run *= alpha;
     l_rnd *= alpha;
-    if (ATTN_FWD_MFMA_LSUM) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc_l[r] *= alpha;
-    }
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -340,7 +309,7 @@ fwd_bf16_kernel(FwdKernelArgs a) {
         a4[(2 * w) & 3] += p0;
         a4[(2 * w + 1) & 3] += p1;
         pt[t][w] = pack_bf16x2(p0, p1);
-        if (!ATTN_FWD_MFMA_LSUM) r2[w & 1] = sum_bf16x2(pt[t][w], r2[w & 1]);
+        r2[w & 1] = sum_bf16x2(pt[t][w], r2[w & 1]);
       }
     }
     ts = (a4[0] + a4[1]) + (a4[2] + a4[3]);
@@ -378,10 +347,6 @@ fwd_bf16_kernel(FwdKernelArgs a) {
         vf[2] = __builtin_bit_cast(u32x2, hi)[0];
         vf[3] = __builtin_bit_cast(u32x2, hi)[1];
         acc_o[db] = mfma_32x32x16_bf16(vf, pt[t], acc_o[db]);
-      }
-      if (ATTN_FWD_MFMA_LSUM) {
-        const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0 pairs
-        acc_l = mfma_32x32x16_bf16(ones, pt[t], acc_l);
       }
     }
   };
@@ -428,22 +393,20 @@ fwd_bf16_kernel(FwdKernelArgs a) {
   // where each wait leaves only the loads of the round's own issue in
   // flight, so every load has landed, in every wave, by the barrier that
   // precedes the first matrix phase reading it.
-  // Order of the matrix phase: each LDS operand read is issued KPRE MFMAs
-  // before the MFMA that consumes it, so LDS latency hides behind matrix
-  // work (0 leaves the order to the compiler).
+  // Order of the matrix phase: each LDS operand read is issued kReadAhead
+  // MFMAs before the MFMA that consumes it, so LDS latency hides behind
+  // matrix work.
   auto matrix_schedule = [&]() __attribute__((always_inline)) {
-    if constexpr (ATTN_FWD_KPRE > 0) matrix_pipeline<0, kNkb * KS, kNt * NDB, ATTN_FWD_KPRE>();
+    matrix_pipeline<0, kNkb * KS, kNt * NDB, kReadAhead>();
   };
 
   auto round = [&](int j, const int P, const bool MASKED, const bool LEAD) __attribute__((always_inline)) {
     const bool more = !MASKED || j + 1 < nkt;  // rounds of the plain loop always have a next tile
     if (LEAD) issue(j, P);
-    prio_matrix();
     // unmasked rounds always need both tiles (j + 1 < nfull <= nneed)
     if (more && (!MASKED || j + 1 < nneed)) scores((P + 1) % kStages);
     if (!MASKED || j < nneed) accumulate(P);
     if (!MASKED) matrix_schedule();
-    prio_vector();
     if (!LEAD) wait_vmem_at_most<kInFlight>();
     lds_barrier();
     if (!LEAD) issue(j + 1, (P + 1) % kStages);
@@ -507,7 +470,7 @@ fwd_bf16_kernel(FwdKernelArgs a) {
   {
     const int qrow = wq0 + n;
     const float lt = sum_halves(l_run);
-    const float lr = ATTN_FWD_MFMA_LSUM ? acc_l[0] : sum_halves(l_rnd);
+    const float lr = sum_halves(l_rnd);
     if (qrow < a.Sq) {
       const float inv = lr > 0.f ? 1.f / lr : 0.f;
       uint16_t* O = a.o + ((size_t)(b * a.H + hq) * a.Sq + qrow) * D;

@@ -65,8 +65,9 @@ extern "C" {
  * uses the sum of the unrounded fp32 probabilities.
  *
  * Sizes: B, Sq, Sk >= 0 (zero sizes are allowed; B*Sq == 0 is a no-op and a
- * pointer whose tensor is empty may be NULL); H, Hkv >= 1 with H % Hkv == 0;
- * d in {64, 128}.  Pointers must be 16-byte aligned (lse: 4-byte).
+ * pointer whose tensor is empty may be NULL); Sq, Sk <= 2^30 and
+ * d in {64, 128} (else ATTN_ERR_UNSUPPORTED); H, Hkv >= 1 with H % Hkv == 0.
+ * Pointers must be 16-byte aligned (lse: 4-byte).
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int Hkv, int Sq, int Sk, int d,
@@ -227,8 +228,8 @@ size_t attn_bwd_workspace_bytes(int B, int H, int Sq);
  * Accumulation is fp32; the outputs are rounded to bf16 (nearest even).
  * Rows that see no key get dQ = 0 and contribute nothing to dK, dV.  Keys no
  * query sees get dK = dV = 0.  No atomics: results are deterministic.
- * dtype must be ATTN_BF16; d in {64, 128}; causal is bottom-right aligned.
- * Errors as for attn_fwd, plus ATTN_ERR_WORKSPACE.
+ * dtype must be ATTN_BF16; d in {64, 128}; Sq, Sk <= 2^30; causal is
+ * bottom-right aligned.  Errors as for attn_fwd, plus ATTN_ERR_WORKSPACE.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, int Sq,

@@ -77,6 +77,13 @@ def test_fwd_rejects(kw, code):
     assert call_fwd(**kw) == code
 
 
+def test_fwd_and_bwd_reject_more_than_2_30_rows():
+    assert call_fwd(Sq=(1 << 30) + 1, B=0) == bd.ATTN_ERR_UNSUPPORTED
+    assert call_fwd(Sk=(1 << 30) + 1) == bd.ATTN_ERR_UNSUPPORTED
+    assert bd.attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, (1 << 30) + 1, 1, 64, 1, 0.1,
+                       bd.ATTN_BF16, FAKE, 1 << 40, None) == bd.ATTN_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("kw", [dict(B=0), dict(Sq=0), dict(B=0, q=None, o=None, k=None, v=None),
                                 dict(Sq=0, q=None, o=None)])
 def test_fwd_empty_is_a_noop(kw):
@@ -323,3 +330,10 @@ def test_bwd_workspace_and_noop():
     nothing = dict(q=None, k=None, v=None, o=None, do=None, lse=None, dq=None, dk=None, dv=None, ws=None)
     assert call_bwd(B=0, **nothing) == bd.ATTN_OK
     assert call_bwd(Sq=0, Sk=0, **nothing) == bd.ATTN_OK
+
+
+def test_package_exports_every_binding_entry_point():
+    import exact_attention_04_amd as pkg
+    for name in bd.EXPORTED + ("fwd", "bwd", "verify", "verify_tree", "verify_paged", "spec_accept"):
+        assert name in pkg.__all__, name
+        assert getattr(pkg, name) is getattr(bd, name)

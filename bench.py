@@ -78,8 +78,19 @@ def verify_algorithmic_bytes(w, seqlens: np.ndarray) -> int:
     return kv + qo + lse
 
 
-def cpu_baseline(w, max_seconds_hint: float = 20.0) -> dict:
-    """The oracle, as it is, on whole heads of the prefill workload."""
+def max_errors(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: np.ndarray) -> dict:
+    """Largest |O - O_ref| (with |O_ref| there) and |LSE - LSE_ref| over every element."""
+    err_o = np.abs(o_gpu - o_ref)
+    i = np.unravel_index(int(np.argmax(err_o)), err_o.shape)
+    fin = np.isfinite(lse_ref)
+    return {"max_abs_err_o": float(err_o[i]), "abs_o_ref_at_max": float(abs(o_ref[i])),
+            "max_abs_err_lse": float(np.abs(lse_gpu[fin] - lse_ref[fin]).max()) if fin.any() else 0.0,
+            "rows_compared": int(np.prod(lse_ref.shape)), "tolerance": {"o": 2e-2, "lse": 1e-3}}
+
+
+def cpu_baseline(w, o_gpu, lse_gpu) -> tuple:
+    """The oracle, as it is, on every head of the prefill workload; its
+    output is also compared with the GPU's (every row)."""
     from exact_attention_04_amd import synth
     from oracle import ref_attention as ref
 
@@ -87,16 +98,107 @@ def cpu_baseline(w, max_seconds_hint: float = 20.0) -> dict:
     n_heads = w.B * w.H
     q, k, v = synth.prefill_inputs(w, "cpu")
     heads = [(i // w.H, i % w.H) for i in range(n_heads)]
-    qn, kn, vn = synth.to_f64(q[:1 + heads[-1][0]]), synth.to_f64(k[:1 + heads[-1][0]]), synth.to_f64(v[:1 + heads[-1][0]])
+    qn, kn, vn = synth.to_f64(q), synth.to_f64(k), synth.to_f64(v)
     log(f"cpu baseline: oracle on {n_heads} heads x {w.Sq} rows with {cores} threads")
     t0 = time.perf_counter()
-    ref.attention(qn, kn, vn, w.causal, w.scale, heads=heads, workers=cores)
+    o_ref, lse_ref = ref.attention(qn, kn, vn, w.causal, w.scale, heads=heads, workers=cores)
     dt = time.perf_counter() - t0
     flops = n_heads * (2.0 * w.Sq * w.Sk * w.d)  # causal convention: half of 4*S^2*d
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    base = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"all {n_heads} (batch, head) pairs of {w.name}, all {w.Sq} query rows, "
-                      f"fp64 materialised rows, {cores} worker threads; {dt:.1f} s wall; "
+                      f"fp64 materialised rows, {cores} worker threads (one BLAS thread each); {dt:.1f} s wall; "
                       f"causal FLOPs halved like the GPU figure"}
+    return base, max_errors(synth.to_f64(o_gpu), synth.to_f64(lse_gpu), o_ref, lse_ref)
+
+
+def stats_us(us: np.ndarray) -> dict:
+    """Mean, median, p10 and p90 of per-call durations (us)."""
+    return {"us_per_call": round(float(us.mean()), 2), "p10_us": round(float(np.percentile(us, 10)), 2),
+            "p50_us": round(float(np.percentile(us, 50)), 2), "p90_us": round(float(np.percentile(us, 90)), 2),
+            "calls": int(len(us))}
+
+
+def host_info() -> dict:
+    """CPU model, threads available to this process and the ROCm version."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    rocm = None
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        try:
+            with open(path) as f:
+                rocm = f.read().strip()
+                break
+        except OSError:
+            pass
+    try:
+        threads = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        threads = os.cpu_count()
+    return {"cpu_model": model, "cpu_threads_available": threads, "rocm_version": rocm}
+
+
+def parse_amdsmi(text: str) -> dict:
+    """Socket power (W) and the GFX (XCD) clocks (MHz) from `amd-smi metric -p -c` output."""
+    import re
+    power = [float(x) for x in re.findall(r"SOCKET_POWER:\s*([0-9.]+)\s*W", text)]
+    clocks = []
+    lines = text.splitlines()
+    for i, line in enumerate(lines):
+        if re.match(r"\s*GFX_\d+:\s*$", line) and i + 1 < len(lines):
+            m = re.match(r"\s*CLK:\s*([0-9.]+)\s*MHz", lines[i + 1])
+            if m:
+                clocks.append(float(m.group(1)))
+    return {"power_w": power, "gfx_clk_mhz": clocks}
+
+
+def sample_clocks(run_for_s: float, call, stream, sample_at=(2.0, 3.0)) -> dict:
+    """Board power and XCD clocks read with amd-smi while `call` runs back to
+    back for run_for_s seconds (the clocks settle under the power limit after
+    a second or two), or None when amd-smi is not available."""
+    import shutil
+    import subprocess
+    import threading
+    import torch
+    smi = shutil.which("amd-smi")
+    if smi is None:
+        return None
+    texts = []
+
+    def sampler():
+        t0 = time.perf_counter()
+        for t in sample_at:
+            time.sleep(max(0.0, t - (time.perf_counter() - t0)))
+            try:
+                r = subprocess.run([smi, "metric", "-p", "-c", "-g", "0"], capture_output=True, text=True,
+                                   timeout=10)
+                texts.append(r.stdout)
+            except (OSError, subprocess.SubprocessError):
+                pass
+    th = threading.Thread(target=sampler)
+    t0 = time.perf_counter()
+    th.start()
+    n = 0
+    while time.perf_counter() - t0 < run_for_s:
+        for _ in range(20):
+            call()
+            n += 1
+        stream.synchronize()
+    th.join()
+    torch.cuda.synchronize()
+    got = [parse_amdsmi(t) for t in texts]
+    clk = [c for g in got for c in g["gfx_clk_mhz"]]
+    pw = [p for g in got for p in g["power_w"]]
+    if not clk:
+        return None
+    return {"samples": len(got), "calls": n, "gfx_clk_mhz_min": min(clk), "gfx_clk_mhz_mean": round(sum(clk) / len(clk), 1),
+            "gfx_clk_mhz_max": max(clk), "socket_power_w": round(sum(pw) / len(pw), 1) if pw else None}
 
 
 def timed_us(fn, n: int, stream) -> np.ndarray:
@@ -162,23 +264,19 @@ def spec_inputs(B, k, V, dev, seed=12):
     return [torch.from_numpy(a).to(dev) for a in (x, q, p, ua, us)]
 
 
-def oracle_threads() -> int:
-    """Threads the oracle's BLAS calls may use in this process."""
-    from oracle import ref_attention as ref
-    try:
-        return int(os.environ.get("OMP_NUM_THREADS", ""))
-    except ValueError:
-        return ref.default_workers()
-
-
-def cpu_rate(fn, work: float, unit: str, sample: str) -> dict:
-    """The oracle as it is, timed once on the host: work / seconds."""
-    t0 = time.perf_counter()
-    fn()
-    dt = time.perf_counter() - t0
+def cpu_rate(fn, work: float, unit: str, sample: str, threads: int = 1) -> dict:
+    """The oracle as it is, timed once on the host: work / seconds.  With
+    threads == 1 its BLAS calls are held to one thread, so `cores` is what
+    ran; callers that pass threads > 1 run the oracle with that many worker
+    threads of one BLAS thread each."""
+    from oracle.ref_attention import _blas_one_thread
+    with _blas_one_thread():
+        t0 = time.perf_counter()
+        fn()
+        dt = time.perf_counter() - t0
     scale = 1e9 if unit == "GB/s" else 1e12
-    return {"value": round(work / dt / scale, 4), "unit": unit, "cores": oracle_threads(), "kind": "oracle",
-            "sample": f"{sample}; {dt:.2f} s wall"}
+    return {"value": round(work / dt / scale, 4), "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": f"{sample}; {dt:.2f} s wall on {threads} thread{'s' if threads > 1 else ''}"}
 
 
 def extras(dev, wv, vq, caches, vsl, seqlens, max_len, stream, cpu: bool = False) -> dict:
@@ -199,8 +297,8 @@ def extras(dev, wv, vq, caches, vsl, seqlens, max_len, stream, cpu: bool = False
                      device=dev)
     for i in range(5):
         plain(i)
-    us = timed_us(plain, 50, stream)
-    out["verify_back_to_back"] = {"us_per_call": round(float(us.mean()), 2),
+    us = timed_us(plain, 200, stream)
+    out["verify_back_to_back"] = {**stats_us(us),
                                   "roofline": {"bound": "hbm", "achieved": round(vbytes / us.mean() / 1e3, 1),
                                                "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                                "frac": round(vbytes / us.mean() / 1e3 / PEAK_HBM_GBPS, 4),
@@ -226,10 +324,10 @@ def extras(dev, wv, vq, caches, vsl, seqlens, max_len, stream, cpu: bool = False
             binding.verify(sq, kc, vc, ssl, int(slen.max()), scale=w.scale, out=o, lse=lse, workspace=ws)
         for i in range(5):
             seeded(i)
-        us = timed_us(seeded, 50, stream)
+        us = timed_us(seeded, 200, stream)
         sb = verify_algorithmic_bytes(w, slen)
         sweep[f"seed{seed}"] = {"sum_seqlens": int(slen.sum()), "algorithmic_bytes": int(sb),
-                                "us_per_call": round(float(us.mean()), 2),
+                                **stats_us(us),
                                 "GB/s": round(sb / us.mean() / 1e3, 1),
                                 "frac": round(sb / us.mean() / 1e3 / PEAK_HBM_GBPS, 4)}
         del sq, sk, sv, ssl, rot
@@ -243,9 +341,9 @@ def extras(dev, wv, vq, caches, vsl, seqlens, max_len, stream, cpu: bool = False
         binding.verify_paged(vq, kp, vp, table, vsl, max_len, scale=wv.scale, out=o, lse=lse, workspace=ws)
     for i in range(5):
         paged(i)
-    us = timed_us(paged, 50, stream)
+    us = timed_us(paged, 200, stream)
     pbytes = vbytes + int(sum((int(s) + 63) // 64 for s in seqlens)) * 4
-    out["verify_paged"] = {"page": 64, "us_per_call": round(float(us.mean()), 2),
+    out["verify_paged"] = {"page": 64, **stats_us(us),
                            "roofline": {"bound": "hbm", "achieved": round(pbytes / us.mean() / 1e3, 1),
                                         "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                         "frac": round(pbytes / us.mean() / 1e3 / PEAK_HBM_GBPS, 4),
@@ -266,8 +364,8 @@ def extras(dev, wv, vq, caches, vsl, seqlens, max_len, stream, cpu: bool = False
         binding.verify_tree(vq, kc, vc, vsl, max_len, tm, scale=wv.scale, out=o, lse=lse, workspace=ws)
     for i in range(5):
         tree(i)
-    us = timed_us(tree, 50, stream)
-    out["verify_tree"] = {"us_per_call": round(float(us.mean()), 2),
+    us = timed_us(tree, 200, stream)
+    out["verify_tree"] = {**stats_us(us),
                           "roofline": {"bound": "hbm", "achieved": round(vbytes / us.mean() / 1e3, 1),
                                        "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                        "frac": round(vbytes / us.mean() / 1e3 / PEAK_HBM_GBPS, 4),
@@ -290,12 +388,12 @@ def extras(dev, wv, vq, caches, vsl, seqlens, max_len, stream, cpu: bool = False
             n_acc.append(n)
     for i in range(5):
         spec(i)
-    us = timed_us(spec, 50, stream)
+    us = timed_us(spec, 200, stream)
     # bytes: the sampled row of p (and of q after a rejection) for every
     # sequence, plus the k looked-up entries; averaged over the two sets
     acc = [a.cpu().numpy() for a in n_acc]
     sbytes = float(np.mean([sum(V * 4 * (2 if j < k else 1) + k * 16 for j in a.tolist()) for a in acc]))
-    out["spec_accept"] = {"B": B, "k": k, "V": V, "us_per_call": round(float(us.mean()), 2),
+    out["spec_accept"] = {"B": B, "k": k, "V": V, **stats_us(us),
                           "roofline": {"bound": "hbm", "achieved": round(sbytes / us.mean() / 1e3, 1),
                                        "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                        "frac": round(sbytes / us.mean() / 1e3 / PEAK_HBM_GBPS, 4),
@@ -327,18 +425,20 @@ def backward_leg(dev, wp, q, k, v, o, lse, stream, cpu: bool = False) -> dict:
     us = timed_us(bwd, 10, stream)
     flops = 2.5 * wp.flops()
     tf = flops / (us.mean() * 1e-6) / 1e12
-    out = {"workload": wp.name, "us_per_call": round(float(us.mean()), 1),
+    out = {"workload": wp.name, **stats_us(us),
            "algorithmic_flops": flops,
            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("backward")}}
     if cpu:
         from oracle import ref_attention as ref
-        one = (slice(0, 1), slice(0, 1))
-        qn, kn, vn, dn = (synth.to_f64(t[one]) for t in (q, k, v, do))
+        n = min(16, ref.default_workers())
+        part = (slice(0, 1), slice(0, n))  # the first n heads of batch 0
+        qn, kn, vn, dn = (synth.to_f64(t[part]) for t in (q, k, v, do))
         out["cpu_baseline"] = cpu_rate(
-            lambda: ref.attention_backward(qn, kn, vn, dn, True, wp.scale), flops / (wp.B * wp.H), "TFLOP/s",
-            f"one (batch, head) pair of {wp.name}: all {wp.Sq} rows, fp64 materialised S, P, dP, dS; rated by "
-            f"that head's share of the algorithmic FLOPs")
+            lambda: ref.attention_backward(qn, kn, vn, dn, True, wp.scale, workers=n), flops * n / (wp.B * wp.H),
+            "TFLOP/s",
+            f"{n} (batch, head) pairs of {wp.name}: all {wp.Sq} rows, fp64 materialised S, P, dP, dS; rated by "
+            f"those heads' share of the algorithmic FLOPs", threads=n)
     return out
 
 
@@ -361,7 +461,7 @@ def other_prefill(dev, stream) -> dict:
             call(i)
         us = timed_us(call, 20, stream)
         tf = w.flops() / (us.mean() * 1e-6) / 1e12
-        e = {"us_per_call": round(float(us.mean()), 2), "TFLOP/s": round(tf, 2)}
+        e = {**stats_us(us), "TFLOP/s": round(tf, 2)}
         if w.dtype == "bf16":
             e["roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}
@@ -383,10 +483,10 @@ def profile_leg(args, dev) -> int:
         for _ in range(n):
             dst.copy_(src)
     elif args.only == "prefill":
-        w = synth.CAUSAL_BF16_S8192
+        w = {x.name: x for x in synth.PREFILL_WORKLOADS}[args.workload]
         q, k, v = synth.prefill_inputs(w, dev)
         for _ in range(n):
-            binding.fwd(q, k, v, causal=True, scale=w.scale)
+            binding.fwd(q, k, v, causal=w.causal, scale=w.scale)
     elif args.only == "backward":
         w = synth.CAUSAL_BF16_S8192
         q, k, v = synth.prefill_inputs(w, dev)
@@ -415,6 +515,8 @@ def main() -> int:
     ap.add_argument("--only", choices=["prefill", "verify", "backward", "copy"], default=None,
                     help="profiling aid: run just one leg (no JSON line); 'copy' runs a plain "
                          "1 GiB device-to-device copy used to calibrate the HBM byte counters")
+    ap.add_argument("--workload", default="causal_bf16_b4h32s8192d128",
+                    help="with --only prefill: the prefill workload to run (by name)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the attention path "
@@ -475,6 +577,8 @@ def main() -> int:
 
     pre_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     ver_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    # clocks and board power while the prefill runs back to back (amd-smi)
+    clocks = sample_clocks(4.0, prefill, stream)
     flops = wp.flops()
     tflops = flops / (pre_ms.mean() * 1e-3) / 1e12
     vbytes = verify_algorithmic_bytes(wv, seqlens)
@@ -506,12 +610,14 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("prefill")},
-        "verify": {"value": round(gbps, 1), "unit": "GB/s", "us_per_call": round(ver_ms.mean() * 1e3, 2),
+        "prefill_stats": stats_us(pre_ms * 1e3),
+        "verify": {"value": round(gbps, 1), "unit": "GB/s", **stats_us(ver_ms * 1e3),
                    "algorithmic_bytes": vbytes,
                    "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                 "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": measured_traffic("verify")}},
         "prefill_ms": round(float(pre_ms.mean()), 4),
-        "device": {"name": props.name, "cus": props.multi_processor_count},
+        "device": {"name": props.name, "cus": props.multi_processor_count, "clocks_under_prefill": clocks},
+        "host": host_info(),
     }
     out["extras"] = extras(dev, wv, vq, caches, vsl, seqlens, max_len, stream, cpu=not args.no_cpu_baseline)
     for name, e in out["extras"].items():
@@ -528,7 +634,11 @@ def main() -> int:
     for name, e in po.items():
         log(f"{name}: {e['us_per_call']:.1f} us -> {e['TFLOP/s']:.1f} TFLOP/s")
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wp)
+        out["cpu_baseline"], out["parity"] = cpu_baseline(wp, o, lse)
+        from oracle import ref_attention as ref
+        vo_ref, vl_ref = ref.verify(synth.to_f64(vq), synth.to_f64(vk), synth.to_f64(vv), seqlens, wv.scale)
+        out["verify"]["parity"] = max_errors(synth.to_f64(vo), synth.to_f64(vlse), vo_ref, vl_ref)
+        log(f"parity (every row): prefill {out['parity']}; verify {out['verify']['parity']}")
     print(json.dumps(out), flush=True)
     return 0
 

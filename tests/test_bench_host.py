@@ -32,3 +32,32 @@ def test_verify_algorithmic_bytes():
     kv = int(sl.sum()) * w.Hkv * w.d * 2 * 2
     assert b == kv + 2 * w.B * w.H * w.kq * w.d * 2 + w.B * w.H * w.kq * 4
     assert b == 413766656  # the seed-4 workload's 413.77 MB
+
+
+def test_parse_amdsmi_reads_power_and_every_xcd_clock():
+    text = "GPU: 0\n    POWER:\n        SOCKET_POWER: 1360 W\n    CLOCK:\n" + "".join(
+        f"        GFX_{i}:\n            CLK: {1800 + i} MHz\n            MIN_CLK: 500 MHz\n"
+        f"            MAX_CLK: 2400 MHz\n" for i in range(8)) + "        MEM_0:\n            CLK: 1900 MHz\n"
+    got = bench.parse_amdsmi(text)
+    assert got["power_w"] == [1360.0]
+    assert got["gfx_clk_mhz"] == [1800.0 + i for i in range(8)]  # MIN/MAX and memory clocks excluded
+
+
+def test_stats_and_max_errors():
+    st = bench.stats_us(np.arange(1.0, 101.0))
+    assert st["calls"] == 100 and st["p50_us"] == 50.5 and st["p10_us"] < st["p50_us"] < st["p90_us"]
+    o_ref = np.zeros((1, 2, 3, 4))
+    o = o_ref.copy()
+    o[0, 1, 2, 3] = 0.01
+    o_ref[0, 1, 2, 3] = -3.0
+    lse_ref = np.array([[[0.0, -np.inf, 1.0], [2.0, 3.0, 4.0]]])
+    lse = lse_ref + 1e-4
+    e = bench.max_errors(o, lse, o_ref, lse_ref)
+    assert abs(e["max_abs_err_o"] - 3.01) < 1e-12 and e["abs_o_ref_at_max"] == 3.0
+    assert abs(e["max_abs_err_lse"] - 1e-4) < 1e-12 and e["rows_compared"] == 6
+
+
+def test_host_info_names_the_cpu():
+    h = bench.host_info()
+    assert h["cpu_threads_available"] >= 1
+    assert h["cpu_model"] is None or isinstance(h["cpu_model"], str)

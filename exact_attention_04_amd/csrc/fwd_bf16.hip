@@ -38,6 +38,10 @@
 //     that computes the tile max, raises m_ref, rescales the accumulator and
 //     exponentiates again.  Probabilities stay below 2^32, far from fp32 and
 //     bf16 overflow, and most tiles need neither a max nor a rescale;
+//   * the output of a wave's 32 rows is staged in LDS (the tile buffers are
+//     free by then) and written back as whole rows, so every store
+//     instruction covers 1 KB of consecutive memory rather than 8 bytes of
+//     32 rows;
 //   * two denominators are kept: the fp32 sum of the probabilities (for LSE)
 //     and the sum of the same probabilities rounded to bf16, i.e. of exactly
 //     the weights the P.V product used (one v_dot2 per pair).  O is divided by
@@ -457,6 +461,7 @@ fwd_bf16_kernel(FwdKernelArgs a) {
     }
     if (LEAD) lds_barrier();  // the trailing group's last barrier
     wait_vmem_all();          // the zero-filling loads past the end
+    lds_barrier();            // every wave's loads have landed: the tile buffers are free
   };
 
   if (nkt > 0) {
@@ -466,26 +471,41 @@ fwd_bf16_kernel(FwdKernelArgs a) {
       run(false);
   }
 
-  // ---- epilogue: one normalised write per row
+  // ---- epilogue: one normalised write per row.  The wave stages its 32
+  // rows of O (bf16) in its own 32*D-element part of the free tile buffers,
+  // 16-byte chunks XOR-swizzled by row, then writes them back as whole rows:
+  // each store instruction covers 1 KB of consecutive output.
   {
     const int qrow = wq0 + n;
     const float lt = sum_halves(l_run);
     const float lr = sum_halves(l_rnd);
-    if (qrow < a.Sq) {
-      const float inv = lr > 0.f ? 1.f / lr : 0.f;
-      uint16_t* O = a.o + ((size_t)(b * a.H + hq) * a.Sq + qrow) * D;
+    const float inv = lr > 0.f ? 1.f / lr : 0.f;
+    uint16_t* stage = (wave >> 1) == 0 ? k_lds0 : (wave >> 1) == 1 ? k_lds1 : (wave >> 1) == 2 ? v_lds0 : v_lds1;
+    stage += (wave & 1) * 32 * D;
+    typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+    typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          // registers 4*rg .. 4*rg+3: head dims 32*db + 8*rg + 4*h + 0..3
-          const uint32_t w0 = pack_bf16x2(acc_o[db][4 * rg + 0] * inv, acc_o[db][4 * rg + 1] * inv);
-          const uint32_t w1 = pack_bf16x2(acc_o[db][4 * rg + 2] * inv, acc_o[db][4 * rg + 3] * inv);
-          *reinterpret_cast<u32x2*>(O + 32 * db + 8 * rg + 4 * h) = u32x2{w0, w1};
-        }
-      if (a.lse != nullptr && h == 0) {
-        a.lse[(size_t)(b * a.H + hq) * a.Sq + qrow] = lt > 0.f ? (m_ref + fast_log2(lt)) * kLn2 : -INFINITY;
+      for (int rg = 0; rg < 4; ++rg) {
+        // registers 4*rg .. 4*rg+3: head dims 32*db + 8*rg + 4*h + 0..3 of row n
+        const uint32_t w0 = pack_bf16x2(acc_o[db][4 * rg + 0] * inv, acc_o[db][4 * rg + 1] * inv);
+        const uint32_t w1 = pack_bf16x2(acc_o[db][4 * rg + 2] * inv, acc_o[db][4 * rg + 3] * inv);
+        const int chunk = (4 * db + rg) ^ (n & (CPR - 1));
+        *reinterpret_cast<lds_u32x2*>((__attribute__((address_space(3))) char*)stage + n * D * 2 + chunk * 16 + 8 * h) =
+            u32x2{w0, w1};
       }
+    if (a.lse != nullptr && h == 0 && qrow < a.Sq)
+      a.lse[(size_t)(b * a.H + hq) * a.Sq + qrow] = lt > 0.f ? (m_ref + fast_log2(lt)) * kLn2 : -INFINITY;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's staging writes are done
+    uint16_t* O = a.o + ((size_t)(b * a.H + hq) * a.Sq + wq0) * D;
+    constexpr int ROWS_PER_STORE = 1024 / (D * 2);
+#pragma unroll
+    for (int i = 0; i < 32 / ROWS_PER_STORE; ++i) {
+      const int r = i * ROWS_PER_STORE + lane / CPR, c = lane % CPR;
+      const u32x4 val = *reinterpret_cast<const lds_u32x4*>(
+          (const __attribute__((address_space(3))) char*)stage + r * D * 2 + ((c ^ (r & (CPR - 1))) * 16));
+      if (wq0 + r < a.Sq) store16(O + (size_t)r * D + c * 8, val);
     }
   }
 }

@@ -143,13 +143,14 @@ fwd_bf16_kernel(FwdKernelArgs a) {
   const bool lead = wave < 4;
   const int rb = 2 * (wave & 3) + (lead ? 0 : 1);
 
-  // Workgroup i runs on XCD i % 8, each XCD taking its ids in order.  Every
-  // XCD gets a contiguous range of heads.  When a head has at least as many
-  // query blocks as an XCD has CUs, the XCD runs its heads one after the
-  // other, heaviest block first (a head's blocks then share the XCD's L2);
-  // with fewer blocks per head (short sequences) the heads' blocks are
-  // interleaved, all heaviest blocks first, which keeps the causal tail
-  // balanced.
+  // Workgroup order (XCDs, shader engines and the causal tail): with fewer
+  // query blocks per head than an XCD has CUs (short sequences) all of an
+  // XCD's heads are interleaved, heaviest blocks first, which balances the
+  // causal tail and gives every four consecutive ids the same cost;
+  // otherwise causal_block_order, four heads side by side while a head's
+  // K/V is at most 4 MiB (the 32 heads in flight, at most 128 MiB, stay in
+  // the last-level cache; at S = 32768 four heads at once measured 3%
+  // slower than one).
   int bh, qblk;
   {
     constexpr int kXcds = 8, kCusPerXcd = 32;
@@ -159,7 +160,7 @@ fwd_bf16_kernel(FwdKernelArgs a) {
       bh = x * hx + i % hx;
       qblk = a.nqb - 1 - i / hx;
     } else {
-      const int blk = xcd_grouped_block(blockIdx.x, gridDim.x);
+      const int blk = causal_block_order(blockIdx.x, gridDim.x, a.nqb, CAUSAL && (long long)a.Sk * D <= (1 << 20));
       bh = blk / a.nqb;
       qblk = blk - bh * a.nqb;
       if (CAUSAL) qblk = a.nqb - 1 - qblk;  // heaviest query blocks of a head first

@@ -46,6 +46,9 @@ def test_parse_amdsmi_reads_power_and_every_xcd_clock():
 def test_stats_and_max_errors():
     st = bench.stats_us(np.arange(1.0, 101.0))
     assert st["calls"] == 100 and st["p50_us"] == 50.5 and st["p10_us"] < st["p50_us"] < st["p90_us"]
+    # with a block-timed figure, that is the time per call; the per-call mean rides along
+    sb = bench.stats_us(np.arange(1.0, 101.0), 40.0)
+    assert sb["us_per_call"] == 40.0 and sb["per_call_event_mean_us"] == 50.5 and sb["p50_us"] == 50.5
     o_ref = np.zeros((1, 2, 3, 4))
     o = o_ref.copy()
     o[0, 1, 2, 3] = 0.01

@@ -147,10 +147,7 @@ fwd_bf16_kernel(FwdKernelArgs a) {
   // query blocks per head than an XCD has CUs (short sequences) all of an
   // XCD's heads are interleaved, heaviest blocks first, which balances the
   // causal tail and gives every four consecutive ids the same cost;
-  // otherwise causal_block_order, four heads side by side while a head's
-  // K/V is at most 4 MiB (the 32 heads in flight, at most 128 MiB, stay in
-  // the last-level cache; at S = 32768 four heads at once measured 3%
-  // slower than one).
+  // otherwise causal_block_order's head pairs.
   int bh, qblk;
   {
     constexpr int kXcds = 8, kCusPerXcd = 32;
@@ -160,7 +157,7 @@ fwd_bf16_kernel(FwdKernelArgs a) {
       bh = x * hx + i % hx;
       qblk = a.nqb - 1 - i / hx;
     } else {
-      const int blk = causal_block_order(blockIdx.x, gridDim.x, a.nqb, CAUSAL && (long long)a.Sk * D <= (1 << 20));
+      const int blk = causal_block_order(blockIdx.x, gridDim.x, a.nqb, CAUSAL);
       bh = blk / a.nqb;
       qblk = blk - bh * a.nqb;
       if (CAUSAL) qblk = a.nqb - 1 - qblk;  // heaviest query blocks of a head first

@@ -87,12 +87,12 @@ def test_full_size_every_row(name, part):
 
 
 @pytest.mark.parametrize("Sq,Sk", [(8192, 8192), (8000, 8192)])
-def test_heads_side_by_side_order_every_row(Sq, Sk):
-    """32+ query blocks per head and at most 4 MiB of K/V per head: the
-    workgroups of four heads run side by side (the order the 8192 workload
-    uses), here with d = 64, grouped-query heads, a ragged last block and
-    Sq != Sk.  Every row of every head against the oracle."""
-    P.fwd_case(Sq + 64, 1, 32, 8, Sq, Sk, 64, True, "bf16", what="four-heads order")
+def test_head_pairs_order_every_row(Sq, Sk):
+    """32+ query blocks per head: the workgroups run two heads at a time in
+    groups of four ids (the order the 8192 and 32768 workloads use), here
+    with d = 64, grouped-query heads, a ragged last block and Sq != Sk.
+    Every row of every head against the oracle."""
+    P.fwd_case(Sq + 64, 1, 32, 8, Sq, Sk, 64, True, "bf16", what="head-pairs order")
 
 
 # ------------------------------------------------------------------ ragged and edge shapes

@@ -38,6 +38,13 @@
 //     that computes the tile max, raises m_ref, rescales the accumulator and
 //     exponentiates again.  Probabilities stay below 2^32, far from fp32 and
 //     bf16 overflow, and most tiles need neither a max nor a rescale;
+//   * with 32 or more query blocks per head, the lightest quarter of every
+//     head's blocks is handed out at run time: each XCD gets a fixed eighth
+//     of the heavier blocks, and the workgroups launched after those claim
+//     the light blocks from a counter, so XCDs that run faster (their clocks
+//     differ by up to 7% under load) take more of them and all finish
+//     together; which workgroup computes a block does not change its
+//     arithmetic, so the output is the same bit for bit;
 //   * the output of a wave's 32 rows is staged in LDS (the tile buffers are
 //     free by then) and written back as whole rows, so every store
 //     instruction covers 1 KB of consecutive memory rather than 8 bytes of
@@ -48,6 +55,9 @@
 //     the latter, so O is a convex combination of V rows whose weights sum to
 //     one; the bf16 rounding of a dominant weight then cancels instead of
 //     showing up as an error of |v| * 2^-9.
+#include <atomic>
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -78,6 +88,12 @@ struct FwdKernelArgs {
   int H, Hkv, Sq, Sk;
   int nqb;   // query blocks per (batch, head)
   float c2;  // scale * log2(e)
+  // dynamic tail (null pool: every workgroup has a fixed block): the first
+  // nstatic workgroups take the heavier nqb - nlight blocks of every head in
+  // a fixed order; the ndyn workgroups after them claim the nlight lightest
+  // blocks of every head, heaviest first, from the counter *pool
+  unsigned* pool;
+  int nlight, nstatic, ndyn;
 };
 
 // Workgroup barrier for the phase hand-over: this wave's LDS reads have
@@ -146,13 +162,37 @@ fwd_bf16_kernel(FwdKernelArgs a) {
   // Workgroup order (XCDs, shader engines and the causal tail): with fewer
   // query blocks per head than an XCD has CUs (short sequences) all of an
   // XCD's heads are interleaved, heaviest blocks first, which balances the
-  // causal tail and gives every four consecutive ids the same cost;
-  // otherwise causal_block_order's head pairs.
+  // causal tail and gives every four consecutive ids the same cost; with a
+  // pool, causal_block_order's head pairs over the heavier blocks, then the
+  // light blocks claimed from the pool (all heads' blocks of one size next
+  // to each other, heaviest first); otherwise the head pairs over all blocks.
   int bh, qblk;
   {
     constexpr int kXcds = 8, kCusPerXcd = 32;
-    const int nbh = gridDim.x / a.nqb;
-    if (CAUSAL && a.nqb < kCusPerXcd && nbh % kXcds == 0) {
+    if (CAUSAL && a.pool != nullptr) {
+      const int nh = a.nqb - a.nlight;
+      const int nbh = a.nstatic / nh;
+      if ((int)blockIdx.x < a.nstatic) {
+        const int blk = causal_block_order(blockIdx.x, a.nstatic, nh, true);
+        bh = blk / nh;
+        qblk = a.nqb - 1 - (blk - bh * nh);
+      } else {
+        // one claim per workgroup; the ndyn-th (last) claimer returns the
+        // counter to zero for the next call that uses it
+        __shared__ int s_claim;
+        if (threadIdx.x == 0) {
+          const unsigned c = __hip_atomic_fetch_add(a.pool, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (c == (unsigned)a.ndyn - 1u) __hip_atomic_store(a.pool, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          s_claim = (int)c;
+        }
+        __syncthreads();
+        const int c = s_claim;
+        if (c >= nbh * a.nlight) return;  // the pool is empty (uniform over the workgroup)
+        bh = c % nbh;
+        qblk = a.nlight - 1 - c / nbh;
+      }
+    } else if (CAUSAL && a.nqb < kCusPerXcd && (gridDim.x / a.nqb) % kXcds == 0) {
+      const int nbh = gridDim.x / a.nqb;
       const int x = blockIdx.x % kXcds, i = blockIdx.x / kXcds, hx = nbh / kXcds;
       bh = x * hx + i % hx;
       qblk = a.nqb - 1 - i / hx;
@@ -508,6 +548,78 @@ fwd_bf16_kernel(FwdKernelArgs a) {
   }
 }
 
+// ---- counters of the dynamic tail.  kPoolSlots counters per GPU in a
+// static device array (zero when the library loads), one 128-byte line
+// each.  Every call that uses one takes the next slot in turn, waits on the
+// GPU for the previous call that used that slot (a HIP event recorded after
+// it), and its last claiming workgroup leaves the counter at zero again; so
+// no two calls ever share a counter, whatever streams they run on.  Calls
+// being captured into a graph use the fixed order instead (a captured call
+// would reuse its slot at every replay without the wait).  The array's
+// address on each device is looked up once with hipGetSymbolAddress.
+constexpr int kPoolSlots = 64;
+constexpr int kPoolStride = 32;  // unsigned ints per slot
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned fwd_pool[kPoolSlots * kPoolStride];
+
+struct PoolState {
+  std::mutex mu;
+  unsigned* base = nullptr;
+  unsigned next = 0;
+  hipEvent_t done[kPoolSlots] = {};
+};
+PoolState g_pool[kMaxDevices];
+
+// Launches the kernel for `a` on stream s, with a pool slot when the shape
+// has a dynamic tail and the stream is not capturing.
+template <int D, bool CAUSAL>
+hipError_t launch_with_pool(FwdKernelArgs a, long long grid_static, int npool, hipStream_t s) {
+  auto plain = [&]() {
+    a.pool = nullptr;
+    a.nlight = a.nstatic = a.ndyn = 0;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid_static), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  };
+  if (npool == 0) return plain();
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) {
+    (void)hipGetLastError();
+    return plain();
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return plain();
+  }
+  PoolState& ps = g_pool[dev];
+  std::lock_guard<std::mutex> lock(ps.mu);
+  if (ps.base == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(fwd_pool)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return plain();
+    }
+    ps.base = static_cast<unsigned*>(p);
+  }
+  const int slot = (int)(ps.next++ % kPoolSlots);
+  hipError_t e = hipSuccess;
+  if (ps.done[slot] == nullptr) {
+    e = hipEventCreateWithFlags(&ps.done[slot], hipEventDisableTiming);
+  } else {
+    e = hipStreamWaitEvent(s, ps.done[slot], 0);
+  }
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return plain();  // nothing was launched on this slot
+  }
+  a.pool = ps.base + (size_t)slot * kPoolStride;
+  a.ndyn = npool + npool / 4;  // a quarter more claimers than blocks: the fastest XCDs may take more
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)(a.nstatic + a.ndyn)), dim3(kThreads), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return hipEventRecord(ps.done[slot], s);
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& p, hipStream_t s) {
   FwdKernelArgs a;
@@ -522,9 +634,17 @@ hipError_t launch(const FwdArgs& p, hipStream_t s) {
   a.Sk = p.Sk;
   a.nqb = (p.Sq + kBr - 1) / kBr;
   a.c2 = p.scale * kLog2e;
-  const long long grid = (long long)p.B * p.H * a.nqb;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  const long long nbh = (long long)p.B * p.H;
+  const long long grid = nbh * a.nqb;
+  // the dynamic tail needs the head-pair order over the heavier blocks:
+  // heads in pairs on every XCD and an even number of heavier blocks
+  int npool = 0;
+  if (CAUSAL && a.nqb >= 32 && a.nqb % 8 == 0 && nbh % 16 == 0) {
+    a.nlight = a.nqb / 4;
+    a.nstatic = (int)(nbh * (a.nqb - a.nlight));
+    npool = (int)(nbh * a.nlight);
+  }
+  return launch_with_pool<D, CAUSAL>(a, grid, npool, s);
 }
 
 }  // namespace

@@ -68,6 +68,16 @@ extern "C" {
  * pointer whose tensor is empty may be NULL); Sq, Sk <= 2^30 and
  * d in {64, 128} (else ATTN_ERR_UNSUPPORTED); H, Hkv >= 1 with H % Hkv == 0.
  * Pointers must be 16-byte aligned (lse: 4-byte).
+ *
+ * Work order: in a bf16 causal call with at least 32 blocks of 256 query
+ * rows per head (a multiple of 8) and B*H a multiple of 16, the lightest
+ * quarter of every head's blocks is handed out at run time through a counter
+ * in a small static device array of the library (64 counters per GPU, taken
+ * in turn; a call waits, on the GPU, for the previous call that used its
+ * counter, so calls on different streams never share one).  A call made
+ * while its stream is being captured into a graph uses a fixed order
+ * instead.  O and lse are bit-for-bit the same either way.  The stream must
+ * belong to the current device.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int Hkv, int Sq, int Sk, int d,

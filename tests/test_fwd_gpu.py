@@ -95,6 +95,74 @@ def test_head_pairs_order_every_row(Sq, Sk):
     P.fwd_case(Sq + 64, 1, 32, 8, Sq, Sk, 64, True, "bf16", what="head-pairs order")
 
 
+# ------------------------------------------------------------------ the dynamic tail
+# With 32+ query blocks per head the lightest quarter of the blocks is claimed
+# from a per-GPU counter at run time; a call captured into a graph uses the
+# fixed order instead.  Which workgroup computes a block changes nothing in
+# its arithmetic, so the two orders must agree bit for bit.
+def _dyn_case(seed, H=32):
+    q, k, v = synth.random_qkv(seed, 1, H, H, 8192, 8192, 128, "bf16", device="cuda")
+    return q, k, v, float(np.float32(128 ** -0.5))
+
+
+def test_dynamic_tail_equals_captured_fixed_order():
+    from exact_attention_04_amd import binding
+    q, k, v, scale = _dyn_case(31)
+    o_d, l_d = binding.fwd(q, k, v, causal=True, scale=scale)  # eager: the dynamic tail
+    torch.cuda.synchronize()
+    o_g = torch.full_like(q, float("nan"))
+    l_g = torch.full((1, 32, 8192), float("nan"), dtype=torch.float32, device="cuda")
+    binding.fwd(q, k, v, causal=True, scale=scale, out=o_g, lse=l_g)  # warm up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        binding.fwd(q, k, v, causal=True, scale=scale, out=o_g, lse=l_g)  # captured: the fixed order
+    for rep in range(3):
+        o_g.fill_(float("nan"))
+        l_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        P.log(f"[fwd] graph replay {rep}")
+        assert torch.equal(o_g, o_d) and torch.equal(l_g, l_d), rep
+        o_e, l_e = binding.fwd(q, k, v, causal=True, scale=scale)  # eager work between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(o_e, o_d) and torch.equal(l_e, l_d), rep
+    P.check_fwd(q, k, v, o_d, l_d, True, scale, "bf16", rows=list(range(0, 8192, 97)) + [8191],
+                what="dynamic tail")
+
+
+def test_dynamic_tail_concurrent_streams():
+    """Calls on two streams at once, more calls than the counter has slots:
+    every result equals that of a call made alone."""
+    from exact_attention_04_amd import binding
+    cases = [_dyn_case(41, H=16), _dyn_case(42, H=16)]
+    refs = []
+    for q, k, v, scale in cases:
+        o, l = binding.fwd(q, k, v, causal=True, scale=scale)
+        torch.cuda.synchronize()
+        refs.append((o, l))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[(torch.empty_like(c[0]), torch.empty((1, 16, 8192), dtype=torch.float32, device="cuda"))
+             for _ in range(4)] for c in cases]
+    n = 80
+    torch.cuda.synchronize()
+    for i in range(n):
+        for j in (0, 1):
+            q, k, v, scale = cases[j]
+            o, l = outs[j][i % 4]
+            with torch.cuda.stream(streams[j]):
+                binding.fwd(q, k, v, causal=True, scale=scale, out=o, lse=l)
+        if i % 4 == 3:
+            torch.cuda.synchronize()
+            for j in (0, 1):
+                for o, l in outs[j]:
+                    assert torch.equal(o, refs[j][0]) and torch.equal(l, refs[j][1]), (i, j)
+                    o.fill_(float("nan"))
+            torch.cuda.synchronize()  # the fills are done before the next calls write
+    P.log(f"[fwd] {2 * n} calls on two streams, every result bitwise equal to a lone call")
+
+
 # ------------------------------------------------------------------ ragged and edge shapes
 EDGE_S = [1, 2, 17, 63, 64, 65, 127, 129, 1000]
 

@@ -51,3 +51,40 @@ def test_noalloc_twice_second_smaller():
     ks = synth.normal(rng, (3, 8, 3000, 128), "bf16").cuda()
     vs = synth.normal(rng, (3, 8, 3000, 128), "bf16").cuda()
     check_against_workspace_call(qs, ks, vs, lengths, w.scale, "smaller")
+
+
+def test_noalloc_in_a_captured_graph():
+    """The callers this entry point is for: a call captured into a HIP graph
+    (it allocates nothing, so capture needs no memory pool), replayed three
+    times with eager work in between; every replay equals the eager
+    workspace call bit for bit."""
+    from exact_attention_04_amd import binding as bd
+    w = synth.VERIFY_BF16
+    q, k, v, sl = synth.verify_inputs(w, "cuda")
+    max_len = int(sl.max())
+    o_w, l_w = bd.verify(q, k, v, sl, max_len, scale=w.scale)
+    torch.cuda.synchronize()
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((w.B, w.H, w.kq), float("nan"), dtype=torch.float32, device="cuda")
+
+    def call():
+        rc = bd.attn_verify_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), sl.data_ptr(), max_len, k.shape[2],
+                                    o.data_ptr(), lse.data_ptr(), w.B, w.H, w.Hkv, w.kq, w.d, w.scale, bd.ATTN_BF16,
+                                    torch.cuda.current_stream().cuda_stream)
+        assert rc == bd.ATTN_OK, bd.attn_strerror(rc)
+    call()  # the first call on the device locates the static scratch: outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for rep in range(3):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        P.log(f"[noalloc] graph replay {rep}")
+        assert torch.equal(o, o_w) and torch.equal(lse, l_w), rep
+        o_e, l_e = bd.verify(q, k, v, sl, max_len, scale=w.scale)  # eager work between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(o_e, o_w) and torch.equal(l_e, l_w), rep

@@ -33,6 +33,7 @@
 //     accumulators in AGPRs and tracks every matrix-core wait state itself.
 #include "device_common.h"
 #include "launch.h"
+#include "tail_pool.h"
 
 namespace attn {
 namespace {
@@ -57,6 +58,12 @@ struct BwdKArgs {
   int nkb;   // key blocks of the dK/dV kernel per (batch, KV head)
   float c2;  // scale * log2(e)
   float scale;
+  // dynamic tails (null: every workgroup has a fixed block): the first
+  // nstatic_* workgroups take the heavier blocks of every (batch, head), the
+  // ndyn_* after them claim the nlight_* lightest blocks from the counter
+  unsigned* tail_q;   // bwd_dq: query blocks
+  unsigned* tail_kv;  // bwd_dkdv: key blocks
+  int nlight_q, nstatic_q, ndyn_q, nlight_kv, nstatic_kv, ndyn_kv;
 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __builtin_bit_cast(float, x << 16); }
@@ -104,10 +111,28 @@ bwd_dq(BwdKArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
-  const int blk = xcd_grouped_block(blockIdx.x, gridDim.x);
-  const int bh = blk / a.nqb;
-  int qblk = blk - bh * a.nqb;
-  if (CAUSAL) qblk = a.nqb - 1 - qblk;
+  // heaviest query blocks first, each XCD a contiguous range of heads; with a
+  // dynamic tail the lightest quarter of every head's blocks goes last,
+  // claimed at run time by whichever XCD gets there first (tail_pool.h)
+  int bh, qblk;
+  if (CAUSAL && a.tail_q != nullptr) {
+    const int nh = a.nqb - a.nlight_q, nbh = a.nstatic_q / nh;
+    if ((int)blockIdx.x < a.nstatic_q) {
+      const int blk = xcd_grouped_block(blockIdx.x, a.nstatic_q);
+      bh = blk / nh;
+      qblk = a.nqb - 1 - (blk - bh * nh);
+    } else {
+      const int c = claim_tail_block(a.tail_q, a.ndyn_q);
+      if (c >= nbh * a.nlight_q) return;  // nothing left (uniform over the workgroup)
+      bh = c % nbh;
+      qblk = a.nlight_q - 1 - c / nbh;
+    }
+  } else {
+    const int blk = xcd_grouped_block(blockIdx.x, gridDim.x);
+    bh = blk / a.nqb;
+    qblk = blk - bh * a.nqb;
+    if (CAUSAL) qblk = a.nqb - 1 - qblk;
+  }
   const int b = bh / a.H, hq = bh - b * a.H, g = hq / (a.H / a.Hkv);
   const int q0 = qblk * 128, wq0 = q0 + 32 * wave, shift = a.Sk - a.Sq;
   const int row = wq0 + n;
@@ -316,9 +341,27 @@ bwd_dkdv(BwdKArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
-  const int blk = xcd_grouped_block(blockIdx.x, gridDim.x);
-  const int bg = blk / a.nkb;
-  const int kblk = blk - bg * a.nkb;
+  // key block 0 (seen by every query) first; with a dynamic tail the last
+  // quarter of the key blocks (seen by the fewest queries) goes last,
+  // claimed at run time
+  int bg, kblk;
+  if (CAUSAL && a.tail_kv != nullptr) {
+    const int nh = a.nkb - a.nlight_kv, nbg = a.nstatic_kv / nh;
+    if ((int)blockIdx.x < a.nstatic_kv) {
+      const int blk = xcd_grouped_block(blockIdx.x, a.nstatic_kv);
+      bg = blk / nh;
+      kblk = blk - bg * nh;
+    } else {
+      const int c = claim_tail_block(a.tail_kv, a.ndyn_kv);
+      if (c >= nbg * a.nlight_kv) return;  // nothing left (uniform over the workgroup)
+      bg = c % nbg;
+      kblk = nh + c / nbg;
+    }
+  } else {
+    const int blk = xcd_grouped_block(blockIdx.x, gridDim.x);
+    bg = blk / a.nkb;
+    kblk = blk - bg * a.nkb;
+  }
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int G = a.H / a.Hkv;
   const int k0 = kblk * kKvKeys, wk0 = k0 + 32 * wave, shift = a.Sk - a.Sq;
@@ -560,6 +603,11 @@ bwd_dkdv(BwdKArgs a) {
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The dynamic tails' counters (tail_pool.h): two per slot, the dQ kernel's
+// at the slot's start and the dK/dV kernel's 32 entries later.
+static __device__ __align__(256) unsigned bwd_tail[kTailSlots * kTailStride];
+TailPoolState g_bwd_tail[kTailMaxDevices];
+
 template <int D, bool CAUSAL>
 hipError_t launch(const BwdArgs& p, hipStream_t s) {
   BwdKArgs a;
@@ -584,17 +632,44 @@ hipError_t launch(const BwdArgs& p, hipStream_t s) {
   a.nkb = (p.Sk + kKvKeys - 1) / kKvKeys;
   a.c2 = p.scale * kLog2e;
   a.scale = p.scale;
-  if (rows > 0) {
-    hipLaunchKernelGGL((bwd_dq<D, CAUSAL>), dim3((unsigned)((size_t)p.B * p.H * a.nqb)), dim3(kThreads), 0, s, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if ((size_t)p.B * p.Hkv * p.Sk > 0) {
-    hipLaunchKernelGGL((bwd_dkdv<D, CAUSAL>), dim3((unsigned)((size_t)p.B * p.Hkv * a.nkb)), dim3(kKvThreads), 0, s,
-                       a);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+  a.tail_q = a.tail_kv = nullptr;
+  a.nlight_q = a.nstatic_q = a.ndyn_q = a.nlight_kv = a.nstatic_kv = a.ndyn_kv = 0;
+  // dynamic tails: the lightest quarter of the blocks, where each XCD's
+  // fixed range of heads still holds whole heads
+  const bool tail_q = CAUSAL && a.nqb >= 32 && a.nqb % 4 == 0 && (p.B * p.H) % 8 == 0;
+  const bool tail_kv = CAUSAL && a.nkb >= 16 && a.nkb % 4 == 0 && (p.B * p.Hkv) % 8 == 0;
+  auto run = [&](unsigned* counters) {
+    size_t grid_q = (size_t)p.B * p.H * a.nqb, grid_kv = (size_t)p.B * p.Hkv * a.nkb;
+    if (counters != nullptr && tail_q) {
+      a.tail_q = counters;
+      a.nlight_q = a.nqb / 4;
+      a.nstatic_q = p.B * p.H * (a.nqb - a.nlight_q);
+      const int n = p.B * p.H * a.nlight_q;
+      a.ndyn_q = n + n / 4;  // a quarter more claimers than blocks: faster XCDs may take more
+      grid_q = (size_t)a.nstatic_q + a.ndyn_q;
+    }
+    if (counters != nullptr && tail_kv) {
+      a.tail_kv = counters + 32;
+      a.nlight_kv = a.nkb / 4;
+      a.nstatic_kv = p.B * p.Hkv * (a.nkb - a.nlight_kv);
+      const int n = p.B * p.Hkv * a.nlight_kv;
+      a.ndyn_kv = n + n / 4;
+      grid_kv = (size_t)a.nstatic_kv + a.ndyn_kv;
+    }
+    if (rows > 0) {
+      hipLaunchKernelGGL((bwd_dq<D, CAUSAL>), dim3((unsigned)grid_q), dim3(kThreads), 0, s, a);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if ((size_t)p.B * p.Hkv * p.Sk > 0) {
+      hipLaunchKernelGGL((bwd_dkdv<D, CAUSAL>), dim3((unsigned)grid_kv), dim3(kKvThreads), 0, s, a);
+      return hipGetLastError();
+    }
+    return hipSuccess;
+  };
+  if (!tail_q && !tail_kv) return run(nullptr);
+  return with_tail_slot(
+      g_bwd_tail, [](void** ptr) { return hipGetSymbolAddress(ptr, HIP_SYMBOL(bwd_tail)); }, s, run);
 }
 
 }  // namespace

@@ -144,6 +144,22 @@ __device__ __forceinline__ int xcd_grouped_block(int bid, int nblocks) {
   return (bid % kXcds) * (nblocks / kXcds) + bid / kXcds;
 }
 
+// One claim from a dynamic-tail counter (tail_pool.h) by the whole
+// workgroup; every thread must call it (it synchronises the workgroup).
+// Returns the claim's index.  Exactly nclaim workgroups claim from a counter
+// in one call, so the one that draws index nclaim - 1 is the last, and it
+// returns the counter to zero for the next call that uses it.
+__device__ __forceinline__ int claim_tail_block(unsigned* counter, int nclaim) {
+  __shared__ int s_claim;
+  if (threadIdx.x == 0) {
+    const unsigned c = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (c == (unsigned)nclaim - 1u) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_claim = (int)c;
+  }
+  __syncthreads();
+  return s_claim;
+}
+
 // Order of causal work split into units (heads) of nper blocks each, block
 // 0 of a unit the heaviest; returns unit * nper + block.  Workgroup i runs
 // on XCD i % 8, and each XCD hands its ids, in order, to its four shader

@@ -55,11 +55,9 @@
 //     the latter, so O is a convex combination of V rows whose weights sum to
 //     one; the bf16 rounding of a dominant weight then cancels instead of
 //     showing up as an error of |v| * 2^-9.
-#include <atomic>
-#include <mutex>
-
 #include "device_common.h"
 #include "launch.h"
+#include "tail_pool.h"
 
 namespace attn {
 namespace {
@@ -177,16 +175,7 @@ fwd_bf16_kernel(FwdKernelArgs a) {
         bh = blk / nh;
         qblk = a.nqb - 1 - (blk - bh * nh);
       } else {
-        // one claim per workgroup; the ndyn-th (last) claimer returns the
-        // counter to zero for the next call that uses it
-        __shared__ int s_claim;
-        if (threadIdx.x == 0) {
-          const unsigned c = __hip_atomic_fetch_add(a.pool, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (c == (unsigned)a.ndyn - 1u) __hip_atomic_store(a.pool, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          s_claim = (int)c;
-        }
-        __syncthreads();
-        const int c = s_claim;
+        const int c = claim_tail_block(a.pool, a.ndyn);
         if (c >= nbh * a.nlight) return;  // the pool is empty (uniform over the workgroup)
         bh = c % nbh;
         qblk = a.nlight - 1 - c / nbh;
@@ -548,77 +537,9 @@ fwd_bf16_kernel(FwdKernelArgs a) {
   }
 }
 
-// ---- counters of the dynamic tail.  kPoolSlots counters per GPU in a
-// static device array (zero when the library loads), one 128-byte line
-// each.  Every call that uses one takes the next slot in turn, waits on the
-// GPU for the previous call that used that slot (a HIP event recorded after
-// it), and its last claiming workgroup leaves the counter at zero again; so
-// no two calls ever share a counter, whatever streams they run on.  Calls
-// being captured into a graph use the fixed order instead (a captured call
-// would reuse its slot at every replay without the wait).  The array's
-// address on each device is looked up once with hipGetSymbolAddress.
-constexpr int kPoolSlots = 64;
-constexpr int kPoolStride = 32;  // unsigned ints per slot
-constexpr int kMaxDevices = 64;
-static __device__ __align__(256) unsigned fwd_pool[kPoolSlots * kPoolStride];
-
-struct PoolState {
-  std::mutex mu;
-  unsigned* base = nullptr;
-  unsigned next = 0;
-  hipEvent_t done[kPoolSlots] = {};
-};
-PoolState g_pool[kMaxDevices];
-
-// Launches the kernel for `a` on stream s, with a pool slot when the shape
-// has a dynamic tail and the stream is not capturing.
-template <int D, bool CAUSAL>
-hipError_t launch_with_pool(FwdKernelArgs a, long long grid_static, int npool, hipStream_t s) {
-  auto plain = [&]() {
-    a.pool = nullptr;
-    a.nlight = a.nstatic = a.ndyn = 0;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid_static), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
-  };
-  if (npool == 0) return plain();
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(s, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) {
-    (void)hipGetLastError();
-    return plain();
-  }
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
-    (void)hipGetLastError();
-    return plain();
-  }
-  PoolState& ps = g_pool[dev];
-  std::lock_guard<std::mutex> lock(ps.mu);
-  if (ps.base == nullptr) {
-    void* p = nullptr;
-    if (hipGetSymbolAddress(&p, HIP_SYMBOL(fwd_pool)) != hipSuccess || p == nullptr) {
-      (void)hipGetLastError();
-      return plain();
-    }
-    ps.base = static_cast<unsigned*>(p);
-  }
-  const int slot = (int)(ps.next++ % kPoolSlots);
-  hipError_t e = hipSuccess;
-  if (ps.done[slot] == nullptr) {
-    e = hipEventCreateWithFlags(&ps.done[slot], hipEventDisableTiming);
-  } else {
-    e = hipStreamWaitEvent(s, ps.done[slot], 0);
-  }
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    return plain();  // nothing was launched on this slot
-  }
-  a.pool = ps.base + (size_t)slot * kPoolStride;
-  a.ndyn = npool + npool / 4;  // a quarter more claimers than blocks: the fastest XCDs may take more
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)(a.nstatic + a.ndyn)), dim3(kThreads), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return hipEventRecord(ps.done[slot], s);
-}
+// The dynamic tail's counters (tail_pool.h): one per slot.
+static __device__ __align__(256) unsigned fwd_tail[kTailSlots * kTailStride];
+TailPoolState g_fwd_tail[kTailMaxDevices];
 
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& p, hipStream_t s) {
@@ -636,15 +557,31 @@ hipError_t launch(const FwdArgs& p, hipStream_t s) {
   a.c2 = p.scale * kLog2e;
   const long long nbh = (long long)p.B * p.H;
   const long long grid = nbh * a.nqb;
-  // the dynamic tail needs the head-pair order over the heavier blocks:
-  // heads in pairs on every XCD and an even number of heavier blocks
-  int npool = 0;
-  if (CAUSAL && a.nqb >= 32 && a.nqb % 8 == 0 && nbh % 16 == 0) {
-    a.nlight = a.nqb / 4;
-    a.nstatic = (int)(nbh * (a.nqb - a.nlight));
-    npool = (int)(nbh * a.nlight);
+  a.pool = nullptr;
+  a.nlight = a.nstatic = a.ndyn = 0;
+  // the dynamic tail (the lightest quarter of every head's blocks) needs the
+  // head-pair order over the heavier blocks: heads in pairs on every XCD and
+  // an even number of heavier blocks
+  if (!(CAUSAL && a.nqb >= 32 && a.nqb % 8 == 0 && nbh % 16 == 0)) {
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
   }
-  return launch_with_pool<D, CAUSAL>(a, grid, npool, s);
+  const int nlight = a.nqb / 4;
+  const int npool = (int)(nbh * nlight);
+  return with_tail_slot(
+      g_fwd_tail, [](void** p) { return hipGetSymbolAddress(p, HIP_SYMBOL(fwd_tail)); }, s,
+      [&](unsigned* counters) {
+        long long g = grid;
+        if (counters != nullptr) {
+          a.pool = counters;
+          a.nlight = nlight;
+          a.nstatic = (int)(nbh * (a.nqb - nlight));
+          a.ndyn = npool + npool / 4;  // a quarter more claimers than blocks: faster XCDs may take more
+          g = a.nstatic + a.ndyn;
+        }
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)g), dim3(kThreads), 0, s, a);
+        return hipGetLastError();
+      });
 }
 
 }  // namespace

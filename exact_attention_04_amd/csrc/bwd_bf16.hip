@@ -636,23 +636,24 @@ hipError_t launch(const BwdArgs& p, hipStream_t s) {
   a.nlight_q = a.nstatic_q = a.ndyn_q = a.nlight_kv = a.nstatic_kv = a.ndyn_kv = 0;
   // dynamic tails: the lightest quarter of the blocks, where each XCD's
   // fixed range of heads still holds whole heads
-  const bool tail_q = CAUSAL && a.nqb >= 32 && a.nqb % 4 == 0 && (p.B * p.H) % 8 == 0;
-  const bool tail_kv = CAUSAL && a.nkb >= 16 && a.nkb % 4 == 0 && (p.B * p.Hkv) % 8 == 0;
+  const long long nbh = (long long)p.B * p.H, nbg = (long long)p.B * p.Hkv;
+  const bool tail_q = CAUSAL && a.nqb >= 32 && a.nqb % 4 == 0 && nbh % 8 == 0 && nbh * a.nqb < (1LL << 30);
+  const bool tail_kv = CAUSAL && a.nkb >= 16 && a.nkb % 4 == 0 && nbg % 8 == 0 && nbg * a.nkb < (1LL << 30);
   auto run = [&](unsigned* counters) {
     size_t grid_q = (size_t)p.B * p.H * a.nqb, grid_kv = (size_t)p.B * p.Hkv * a.nkb;
     if (counters != nullptr && tail_q) {
       a.tail_q = counters;
       a.nlight_q = a.nqb / 4;
-      a.nstatic_q = p.B * p.H * (a.nqb - a.nlight_q);
-      const int n = p.B * p.H * a.nlight_q;
+      a.nstatic_q = (int)(nbh * (a.nqb - a.nlight_q));
+      const int n = (int)(nbh * a.nlight_q);
       a.ndyn_q = n + n / 4;  // a quarter more claimers than blocks: faster XCDs may take more
       grid_q = (size_t)a.nstatic_q + a.ndyn_q;
     }
     if (counters != nullptr && tail_kv) {
       a.tail_kv = counters + 32;
       a.nlight_kv = a.nkb / 4;
-      a.nstatic_kv = p.B * p.Hkv * (a.nkb - a.nlight_kv);
-      const int n = p.B * p.Hkv * a.nlight_kv;
+      a.nstatic_kv = (int)(nbg * (a.nkb - a.nlight_kv));
+      const int n = (int)(nbg * a.nlight_kv);
       a.ndyn_kv = n + n / 4;
       grid_kv = (size_t)a.nstatic_kv + a.ndyn_kv;
     }

@@ -562,7 +562,7 @@ hipError_t launch(const FwdArgs& p, hipStream_t s) {
   // the dynamic tail (the lightest quarter of every head's blocks) needs the
   // head-pair order over the heavier blocks: heads in pairs on every XCD and
   // an even number of heavier blocks
-  if (!(CAUSAL && a.nqb >= 32 && a.nqb % 8 == 0 && nbh % 16 == 0)) {
+  if (!(CAUSAL && a.nqb >= 32 && a.nqb % 8 == 0 && nbh % 16 == 0 && grid < (1LL << 30))) {
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
   }

@@ -38,8 +38,9 @@
 //     that computes the tile max, raises m_ref, rescales the accumulator and
 //     exponentiates again.  Probabilities stay below 2^32, far from fp32 and
 //     bf16 overflow, and most tiles need neither a max nor a rescale;
-//   * with 32 or more query blocks per head, the lightest quarter of every
-//     head's blocks is handed out at run time: each XCD gets a fixed eighth
+//   * with 32 or more query blocks per head (a multiple of 8, over a
+//     multiple of 16 heads), the lightest quarter of every head's blocks is
+//     handed out at run time (tail_pool.h): each XCD gets a fixed eighth
 //     of the heavier blocks, and the workgroups launched after those claim
 //     the light blocks from a counter, so XCDs that run faster (their clocks
 //     differ by up to 7% under load) take more of them and all finish

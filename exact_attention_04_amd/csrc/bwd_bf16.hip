@@ -311,16 +311,14 @@ bwd_dq(BwdKArgs a) {
 }
 
 // ---- dK, dV
-#ifndef ATTN_BWD_KV_WAVES
-#define ATTN_BWD_KV_WAVES 8
-#endif
-constexpr int kKvWaves = ATTN_BWD_KV_WAVES;  // 4: one wave per SIMD, V in registers; 8: two, V in LDS
+// Eight waves, two per SIMD, 32 keys each; the V rows of the workgroup's
+// keys sit in LDS (the dK/dV accumulators leave no registers for them).
+constexpr int kKvWaves = 8;
 constexpr int kKvThreads = 64 * kKvWaves;
-constexpr int kKvKeys = 32 * kKvWaves;       // keys per workgroup
-constexpr bool kVinLds = kKvWaves == 8;
+constexpr int kKvKeys = 32 * kKvWaves;  // keys per workgroup
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(kKvWaves / 4, kKvWaves / 4)))
+__global__ void __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dkdv(BwdKArgs a) {
   constexpr int CPR = D / 8, KS = D / 16, NDB = D / 32;
   constexpr int BR = 64;  // query rows per tile
@@ -335,7 +333,7 @@ bwd_dkdv(BwdKArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t d_lds1[TILE];
   __shared__ __attribute__((aligned(256))) float st_lds0[2][BR];  // LSE2, D of the tile's rows
   __shared__ __attribute__((aligned(256))) float st_lds1[2][BR];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[kVinLds ? kKvKeys * D : 1];  // V rows k0 ..
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[kKvKeys * D];  // V rows k0 ..
   typedef const __attribute__((address_space(3))) char lds_cchar;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -370,16 +368,13 @@ bwd_dkdv(BwdKArgs a) {
   const uint16_t* Kg = a.k + (size_t)(b * a.Hkv + g) * a.Sk * D;
   const uint16_t* Vg = a.v + (size_t)(b * a.Hkv + g) * a.Sk * D;
 
-  // K^T (and, with one wave per SIMD, V^T) B operands of this lane's key;
-  // with two waves per SIMD the V rows of the workgroup's keys go to LDS
-  // (rows past Sk read as zeros) and V^T is read from there
-  u32x4 kf[KS], vf[kVinLds ? 1 : KS];
+  // K^T B operands of this lane's key; the V rows of the workgroup's keys
+  // go to LDS (rows past Sk read as zeros) and V^T is read from there
+  u32x4 kf[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
+  for (int ks = 0; ks < KS; ++ks)
     kf[ks] = key_ok ? load16(Kg + (size_t)key * D + ks * 16 + h * 8) : u32x4{0, 0, 0, 0};
-    if constexpr (!kVinLds) vf[ks] = key_ok ? load16(Vg + (size_t)key * D + ks * 16 + h * 8) : u32x4{0, 0, 0, 0};
-  }
-  if constexpr (kVinLds) {
+  {
     const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(Vg + (size_t)k0 * D), (short)0, max(a.Sk - k0, 0) * D * 2, kBufferWord3);
 #pragma unroll
@@ -476,17 +471,13 @@ bwd_dkdv(BwdKArgs a) {
       const u32x4 qa = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(qb_ + ao + blk32 * 32 * D * 2);
       const u32x4 da = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(db_ + ao + blk32 * 32 * D * 2);
       s = mfma_32x32x16_bf16(qa, kf[ks], s);
-      if constexpr (kVinLds) {
-        // row 32 wave + n of the V rows: its swizzle is that of n
-        const u32x4 vt = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-            (lds_cchar*)v_lds + 32 * wave * D * 2 + ao);
-        dp = mfma_32x32x16_bf16(da, vt, dp);
-      } else {
-        dp = mfma_32x32x16_bf16(da, vf[ks], dp);
-      }
+      // row 32 wave + n of the V rows: its swizzle is that of n
+      const u32x4 vt = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+          (lds_cchar*)v_lds + 32 * wave * D * 2 + ao);
+      dp = mfma_32x32x16_bf16(da, vt, dp);
       // two waves per SIMD hide the LDS latency; keep the operands of one
       // step live at a time
-      if constexpr (kVinLds) __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // register r: query row r0 + 32 blk32 + 8(r/4) + 4h + r%4; this lane's key
 #pragma unroll
@@ -550,7 +541,7 @@ bwd_dkdv(BwdKArgs a) {
           qa[3] = __builtin_bit_cast(u32x2, qhi)[1];
           dv[db] = mfma_32x32x16_bf16(da, pp[st], dv[db]);
           dk[db] = mfma_32x32x16_bf16(qa, dsp[st], dk[db]);
-          if constexpr (kVinLds) __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }

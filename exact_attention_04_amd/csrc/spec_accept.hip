@@ -27,8 +27,11 @@
 //             reduce the chunk's fixed-point weights of the distribution to
 //             sample (the residual, or the target's bonus distribution) and of
 //             the target distribution alone (the fallback when the residual
-//             has no mass);
-//   pass 2 -- one workgroup per sequence: scan the chunk sums, find the chunk
+//             has no mass); the chunk-0 workgroup also records the rejection
+//             index for pass 2;
+//   pass 2 -- one workgroup per sequence: load the rejection index and the
+//             chunk sums together (one memory round trip instead of the
+//             dependent loads of the ballot), scan the sums, find the chunk
 //             holding T, scan that chunk and write the outputs.
 // Both passes read the vocabulary rows coalesced; the traffic is one read of
 // the sampled rows.
@@ -53,6 +56,7 @@ struct SpecArgs {
   int32_t* n_acc;        // [B]
   int32_t* tokens;       // [B][k+1]
   long long* sums;       // [B][nchunk][2]: weights to sample, target weights
+  int32_t* first_rej;    // [B]: the first rejected position (k if none), from pass 1
   int B, k, V, nchunk;
 };
 
@@ -116,6 +120,7 @@ __global__ void __launch_bounds__(kThreads) spec_chunk_sums(SpecArgs a) {
   __shared__ long long red[2][kWaves];
   const int c = blockIdx.x, b = blockIdx.y;
   const int j = first_rejection(a, b);
+  if (c == 0 && threadIdx.x == 0) a.first_rej[b] = j;
   const float* prow = a.p + ((size_t)b * (a.k + 1) + j) * a.V;
   const float* qrow = j < a.k ? a.q + ((size_t)b * a.k + j) * a.V : nullptr;
   long long ws = 0, wp = 0;
@@ -157,7 +162,7 @@ __global__ void __launch_bounds__(kThreads) spec_pick(SpecArgs a) {
   __shared__ long long red[kWaves];
   __shared__ long long s_found[2];  // chunk index, running sum before it
   const int b = blockIdx.x, tid = threadIdx.x;
-  const int j = first_rejection(a, b);
+  const int j = a.first_rej[b];  // written by pass 1's chunk-0 workgroup
   const long long* sums = a.sums + (size_t)b * a.nchunk * 2;
   constexpr int kChunksPerThread = 4;  // nchunk <= 1024 (V <= 2^22)
 
@@ -250,10 +255,13 @@ __global__ void __launch_bounds__(kThreads) spec_pick(SpecArgs a) {
 
 }  // namespace
 
-size_t spec_accept_workspace_bytes(int B, int V) {
+// chunk sums, then the rejection indices (16-byte aligned)
+static size_t spec_sums_bytes(int B, int V) {
   const size_t nchunk = ((size_t)V + kChunk - 1) / kChunk;
-  return (size_t)B * nchunk * 2 * sizeof(long long);
+  return ((size_t)B * nchunk * 2 * sizeof(long long) + 15) & ~(size_t)15;
 }
+
+size_t spec_accept_workspace_bytes(int B, int V) { return spec_sums_bytes(B, V) + (size_t)B * sizeof(int32_t); }
 
 hipError_t launch_spec_accept(const SpecAcceptArgs& p, hipStream_t s) {
   SpecArgs a;
@@ -265,6 +273,7 @@ hipError_t launch_spec_accept(const SpecAcceptArgs& p, hipStream_t s) {
   a.n_acc = p.n_accepted;
   a.tokens = p.out_tokens;
   a.sums = static_cast<long long*>(p.workspace);
+  a.first_rej = reinterpret_cast<int32_t*>(static_cast<char*>(p.workspace) + spec_sums_bytes(p.B, p.V));
   a.B = p.B;
   a.k = p.k;
   a.V = p.V;

@@ -256,7 +256,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
 /*
  * attn_spec_accept_workspace_bytes -- bytes of device workspace
  * attn_spec_accept needs: two int64 sums per (sequence, 4096-entry chunk of
- * the vocabulary).  Returns 0 for invalid sizes.
+ * the vocabulary), then one int32 per sequence (its first rejected
+ * position, passed from the first kernel to the second).  Returns 0 for
+ * invalid sizes.
  */
 size_t attn_spec_accept_workspace_bytes(int B, int V);
 

@@ -273,8 +273,10 @@ def test_spec_accept_rejects(kw, code):
 
 
 def test_spec_accept_workspace_and_noop():
-    assert bd.attn_spec_accept_workspace_bytes(8, 4096) == 8 * 1 * 16
-    assert bd.attn_spec_accept_workspace_bytes(8, 4097) == 8 * 2 * 16
+    # two int64 sums per (sequence, 4096-entry chunk), 16-byte aligned, then one int32 per sequence
+    assert bd.attn_spec_accept_workspace_bytes(8, 4096) == 8 * 1 * 16 + 8 * 4
+    assert bd.attn_spec_accept_workspace_bytes(8, 4097) == 8 * 2 * 16 + 8 * 4
+    assert bd.attn_spec_accept_workspace_bytes(3, 4096) == 48 + 3 * 4
     assert bd.attn_spec_accept_workspace_bytes(1, 0) == 0
     assert bd.attn_spec_accept_workspace_bytes(1, (1 << 22) + 1) == 0
     assert call_spec(B=0, x=None, q=None, p=None, ua=None, us=None, n=None, out=None, ws=None) == bd.ATTN_OK

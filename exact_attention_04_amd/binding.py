@@ -266,9 +266,11 @@ def verify_tree(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, s
 
 def spec_accept(draft_tokens: torch.Tensor, draft_probs: torch.Tensor, target_probs: torch.Tensor,
                 u_accept: torch.Tensor, u_sample: torch.Tensor,
-                workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                workspace: Optional[torch.Tensor] = None, n_accepted: Optional[torch.Tensor] = None,
+                out_tokens: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """(n_accepted [B], out_tokens [B, k+1]) of the acceptance rule; draft_tokens [B, k] int32,
-    draft_probs [B, k, V] and target_probs [B, k+1, V] fp32, u_accept [B, k] and u_sample [B] fp32."""
+    draft_probs [B, k, V] and target_probs [B, k+1, V] fp32, u_accept [B, k] and u_sample [B] fp32.
+    The two outputs (int32) are written into n_accepted / out_tokens when given."""
     B, k1, V = target_probs.shape
     k = k1 - 1
     for t, dt in ((draft_tokens, torch.int32), (draft_probs, torch.float32), (target_probs, torch.float32),
@@ -279,8 +281,11 @@ def spec_accept(draft_tokens: torch.Tensor, draft_probs: torch.Tensor, target_pr
             tuple(u_accept.shape) != (B, k) or tuple(u_sample.shape) != (B,):
         raise ValueError("inconsistent shapes")
     dev = target_probs.device
-    n_acc = torch.empty(B, dtype=torch.int32, device=dev)
-    out = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    n_acc = torch.empty(B, dtype=torch.int32, device=dev) if n_accepted is None else n_accepted
+    out = torch.empty((B, k + 1), dtype=torch.int32, device=dev) if out_tokens is None else out_tokens
+    if n_acc.dtype != torch.int32 or tuple(n_acc.shape) != (B,) or out.dtype != torch.int32 or \
+            tuple(out.shape) != (B, k + 1):
+        raise ValueError("outputs must be int32 [B] and [B, k+1]")
     need = attn_spec_accept_workspace_bytes(B, V)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)

@@ -97,3 +97,16 @@ def test_verify_workload_shape():
     vocabulary."""
     n = run_and_check(*make_case(4, 8, 5, 131072, mix=0.8), what="verify-batch")
     assert n.min() >= 0 and n.max() <= 5
+
+
+def test_outputs_written_in_place():
+    """Preallocated output tensors receive the same result as fresh ones."""
+    from exact_attention_04_amd import binding
+    x, q, p, u_acc, u_smp = (torch.from_numpy(a).cuda() for a in make_case(17, 6, 4, 9000))
+    n_a, out_a = binding.spec_accept(x, q, p, u_acc, u_smp)
+    n_b = torch.full((6,), -9, dtype=torch.int32, device="cuda")
+    out_b = torch.full((6, 5), -9, dtype=torch.int32, device="cuda")
+    n_c, out_c = binding.spec_accept(x, q, p, u_acc, u_smp, n_accepted=n_b, out_tokens=out_b)
+    torch.cuda.synchronize()
+    assert n_c is n_b and out_c is out_b
+    assert torch.equal(n_a, n_b) and torch.equal(out_a, out_b)

@@ -10,11 +10,13 @@
 // with D_i = rowsum(dO_i * O_i), which equals sum_j P_ij dP_ij because O = P V.
 //
 // Two kernels, no atomics (deterministic):
-//   * bwd_dq: one workgroup per (batch, head, 128 query rows), like the
-//     forward kernel: each wave holds 32 query rows' Q and dO as MFMA B
-//     operands, computes the rows' D_i and LSE_i * log2(e) (written to the
-//     workspace for the next kernel), K/V tiles of 64 keys stream through
-//     LDS, and per tile
+//   * bwd_dq: one workgroup per (batch, head, 256 query rows), laid out like
+//     the forward kernel (eight waves in two groups one phase apart, so one
+//     wave of every SIMD does matrix work while the other does vector work):
+//     each wave holds 32 query rows' Q and dO as MFMA B operands, computes
+//     the rows' D_i and LSE_i * log2(e) (written to the workspace for the
+//     next kernel), K/V tiles of 32 keys (64 at d = 64) stream through LDS,
+//     and per tile
 //       S^T = K Q^T, dP^T = V dO^T            (scores transposed: lane = query)
 //       dS^T = P^T * (dP^T - D)               (P^T = exp2(S^T c - LSE2))
 //       dQ^T += K^T dS^T                      (K^T by LDS transpose reads);
@@ -38,9 +40,6 @@
 namespace attn {
 namespace {
 
-constexpr int kThreads = 256;  // four waves
-constexpr int kWaves = 4;
-
 struct BwdKArgs {
   const uint16_t* q;     // [B][H][Sq][D]
   const uint16_t* k;     // [B][Hkv][Sk][D]
@@ -54,7 +53,7 @@ struct BwdKArgs {
   uint16_t* dk;
   uint16_t* dv;
   int B, H, Hkv, Sq, Sk;
-  int nqb;   // 128-row query blocks per (batch, head)
+  int nqb;   // query blocks of the dQ kernel per (batch, head)
   int nkb;   // key blocks of the dK/dV kernel per (batch, KV head)
   float c2;  // scale * log2(e)
   float scale;
@@ -93,24 +92,65 @@ __device__ __forceinline__ void lds_sync() {
 }
 
 // ---- dQ
+// Eight waves, 256 query rows, in two groups of four (one wave of each per
+// SIMD) that run one phase apart, as in the forward kernel: per K/V tile a
+// wave has a matrix phase (the scores S^T, dP^T of the next tile and this
+// tile's dQ^T += K^T dS^T, 24 MFMAs at d = 128) and a vector phase (dS^T of
+// the next tile), and workgroup barriers between the phases keep one wave
+// of every SIMD on the matrix core while the other does its vector work.
+// K_j is read in two rounds (the scores of tile j, then dQ_j), so a tile
+// buffer is free again only after the round after its scores; the tiles
+// rotate through four LDS buffers, and the loads of round j fill the buffer
+// of tile j-1 with tile j+3, which round j+2 reads first (three buffers,
+// loads landing within their round, measured 1% slower; five no faster).
+constexpr int kDqWaves = 8;
+constexpr int kDqThreads = 64 * kDqWaves;
+constexpr int kDqRows = 32 * kDqWaves;  // query rows per workgroup
+constexpr int kDqStages = 4;            // LDS buffers per K and V stream
+constexpr int kDqReadAhead = 4;         // MFMAs between an LDS operand read and its use
+
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dq(BwdKArgs a) {
   constexpr int CPR = D / 8, KS = D / 16, NDB = D / 32;
-  constexpr int BC = 64;  // keys per tile
+  // keys per tile: 32 at d = 128, where the scores and dP of a 64-key tile
+  // next to dS, the Q, dO operands and the dQ accumulators would not fit in
+  // the registers; 64 at d = 64
+  constexpr int BC = D == 128 ? 32 : 64;
+  constexpr int NKB = BC / 32, NT = BC / 16;  // 32-key blocks, 16-key MFMA steps per tile
   constexpr int TILE = BC * D;
   constexpr int ROWS_PER_INSN = 1024 / (D * 2);
-  constexpr int IPW = TILE * 2 / 1024 / kWaves;
+  constexpr int IPW = TILE * 2 / 1024 / kDqWaves;
   static_assert(IPW >= 1, "every wave loads part of each tile");
+  // one LDS object per buffer, so the compiler can prove that loads into one
+  // buffer never alias reads of another
+  static_assert(kDqStages >= 3 && kDqStages <= 5, "three to five buffers per stream");
+  constexpr int T3 = kDqStages > 3 ? TILE : 1, T4 = kDqStages > 4 ? TILE : 1;
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds2[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds3[T3];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds4[T4];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds2[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds3[T3];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds4[T4];
+  auto kbuf = [&](const int I) __attribute__((always_inline)) {
+    return I == 0 ? k_lds0 : I == 1 ? k_lds1 : I == 2 ? k_lds2 : I == 3 ? k_lds3 : k_lds4;
+  };
+  auto vbuf = [&](const int I) __attribute__((always_inline)) {
+    return I == 0 ? v_lds0 : I == 1 ? v_lds1 : I == 2 ? v_lds2 : I == 3 ? v_lds3 : v_lds4;
+  };
   typedef const __attribute__((address_space(3))) char lds_cchar;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
+  // waves w and w + 4 share a SIMD; w < 4 leads, w >= 4 trails by one
+  // phase; their row blocks interleave so both groups reach the same last key
+  const bool lead = wave < 4;
+  const int rb = 2 * (wave & 3) + (lead ? 0 : 1);
   // heaviest query blocks first, each XCD a contiguous range of heads; with a
   // dynamic tail the lightest quarter of every head's blocks goes last,
   // claimed at run time by whichever XCD gets there first (tail_pool.h)
@@ -134,7 +174,7 @@ bwd_dq(BwdKArgs a) {
     if (CAUSAL) qblk = a.nqb - 1 - qblk;
   }
   const int b = bh / a.H, hq = bh - b * a.H, g = hq / (a.H / a.Hkv);
-  const int q0 = qblk * 128, wq0 = q0 + 32 * wave, shift = a.Sk - a.Sq;
+  const int q0 = qblk * kDqRows, wq0 = q0 + 32 * rb, shift = a.Sk - a.Sq;
   const int row = wq0 + n;
   const bool row_ok = row < a.Sq;
   const size_t rbase = (size_t)(b * a.H + hq) * a.Sq;
@@ -143,12 +183,19 @@ bwd_dq(BwdKArgs a) {
   const uint16_t* K = uniform_ptr(a.k + (size_t)(b * a.Hkv + g) * a.Sk * D);
   const uint16_t* V = uniform_ptr(a.v + (size_t)(b * a.Hkv + g) * a.Sk * D);
 
+  // tiles the workgroup visits (every wave runs all of them: the phases are
+  // workgroup-wide); tiles [0, nfull) need no mask for this wave's rows, and
+  // tiles from nneed on hold no key any of its rows sees (causal diagonal):
+  // the wave skips their matrix and vector work but takes part in the loads
+  // and barriers
   int kend = a.Sk;
-  if (CAUSAL) kend = min(a.Sk, min(q0 + 128, a.Sq) + shift);
+  if (CAUSAL) kend = min(a.Sk, min(q0 + kDqRows, a.Sq) + shift);
   kend = max(kend, 0);
   const int nkt = (kend + BC - 1) / BC;
-  int nfull = a.Sk / BC;  // tiles [0, nfull) need no mask for this wave's rows
+  int nfull = a.Sk / BC;
   if (CAUSAL) nfull = min(nfull, max(wq0 + shift + 1, 0) / BC);
+  int nneed = nkt;
+  if (CAUSAL) nneed = min(nkt, (max(min(wq0 + 31, a.Sq - 1) + shift + 1, 0) + BC - 1) / BC);
 
   // Q^T and dO^T B operands (column = this lane's row; the two halves of
   // the wave hold alternate 8-value groups of the head dims), and the row
@@ -177,71 +224,118 @@ bwd_dq(BwdKArgs a) {
   const bool live = lse2 != -INFINITY;
   const float lse_use = live ? lse2 : 0.f;
 
-  // HBM -> LDS loads (both tiles in the b_swz layout)
-  uint32_t voff[IPW];
-#pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int r = (wave * IPW + i) * ROWS_PER_INSN + lane / CPR;
-    voff[i] = (r * D + (((lane % CPR) ^ b_swz<D>(r)) * 8)) * 2;
+  // HBM -> LDS loads (both tiles in the b_swz layout); the descriptors end
+  // at the workgroup's last key, so keys past it, and tiles past the last,
+  // read as zeros
+  // Load i of this wave covers tile rows (wave IPW + i) ROWS_PER_INSN +
+  // lane / CPR; their swizzle differs from load 0's only in the bits i sets
+  // (the row's bits 2-3 at d = 128, bit 2 at d = 64), so the lane's offset
+  // is voff0 ^ 16 i plus i whole loads of rows.
+  static_assert(D == 128 ? IPW <= 4 : IPW <= 2, "the swizzle of load i differs from load 0's by i");
+  uint32_t voff0;
+  {
+    const int r = wave * IPW * ROWS_PER_INSN + lane / CPR;
+    voff0 = (r * D + (((lane % CPR) ^ b_swz<D>(r)) * 8)) * 2;
   }
-  auto issue = [&](int t, const int BUF) __attribute__((always_inline)) {
+  auto issue_tile = [&](int t, const int BUF) __attribute__((always_inline)) {
     const int j0 = t * BC;
-    const int bytes = max(a.Sk - j0, 0) * D * 2;
+    const int bytes = max(kend - j0, 0) * D * 2;
     const __amdgpu_buffer_rsrc_t kr =
         __builtin_amdgcn_make_buffer_rsrc((void*)(K + (size_t)j0 * D), (short)0, bytes, kBufferWord3);
     const __amdgpu_buffer_rsrc_t vr =
         __builtin_amdgcn_make_buffer_rsrc((void*)(V + (size_t)j0 * D), (short)0, bytes, kBufferWord3);
-    uint16_t* kd = BUF ? k_lds1 : k_lds0;
-    uint16_t* vd = BUF ? v_lds1 : v_lds0;
+    uint16_t* kd = kbuf(BUF);
+    uint16_t* vd = vbuf(BUF);
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      buffer_load_lds16(kr, kd + (wave * IPW + i) * 512, voff[i]);
-      buffer_load_lds16(vr, vd + (wave * IPW + i) * 512, voff[i]);
+      const uint32_t vo = (voff0 ^ (16 * i)) + i * 1024;
+      buffer_load_lds16(kr, kd + (wave * IPW + i) * 512, vo);
+      buffer_load_lds16(vr, vd + (wave * IPW + i) * 512, vo);
     }
   };
+  // the loads of round j (P = j % S): tile j+S-1 into the buffers of tile
+  // j-1, which round j-1 read for the last time; round j+1 reads tile j+2,
+  // so at the end of round j each wave may leave the loads of its latest
+  // S-3 rounds in flight
+  auto issue = [&](int j, const int P) __attribute__((always_inline)) {
+    issue_tile(j + kDqStages - 1, (P + kDqStages - 1) % kDqStages);
+  };
+  constexpr int kInFlight = (kDqStages - 3) * 2 * IPW;
 
-  // operand offsets: row-major A reads (row n of a 32-key block) and K^T
-  // transpose reads (rows 16t + 4h + r4 and 16t + 8 + 4h + r4, d columns
-  // 32db + 16(gq&1) + 4c4 .. +3)
+  // LDS byte offsets of the operand reads, one register each: row-major A
+  // reads of step ks (row n of a 32-key block) at a_off0 ^ 32 ks, K^T
+  // transpose reads of head-dim block db (rows 16t + 4h + r4 and
+  // 16t + 8 + 4h + r4, d columns 32db + 16(gq&1) + 4c4 .. +3) at
+  // tr_lo0 / tr_hi0 ^ 64 db: the swizzle only permutes chunk bits that the
+  // row term never sets.  An opaque redefinition per round keeps the
+  // compiler from hoisting the XORs into registers of their own.
   const int gq = lane >> 4, r4 = (lane >> 2) & 3, c4 = lane & 3;
-  uint32_t a_off[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) a_off[ks] = (n * D + (((ks * 2 + h) ^ b_swz<D>(n)) * 8)) * 2;
-  uint32_t tr_lo[NDB], tr_hi[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const int dcol = 32 * db + 16 * (gq & 1) + 4 * c4;
+  uint32_t a_off0 = (n * D + ((h ^ b_swz<D>(n)) * 8)) * 2;
+  uint32_t tr_lo0, tr_hi0;
+  {
+    const int dcol = 16 * (gq & 1) + 4 * c4;
     const int rl = 4 * h + r4, rh = 8 + 4 * h + r4;
-    tr_lo[db] = (rl * D + (((dcol >> 3) ^ b_swz<D>(rl)) * 8) + (dcol & 7)) * 2;
-    tr_hi[db] = (rh * D + (((dcol >> 3) ^ b_swz<D>(rh)) * 8) + (dcol & 7)) * 2;
+    tr_lo0 = (rl * D + (((dcol >> 3) ^ b_swz<D>(rl)) * 8) + (dcol & 7)) * 2;
+    tr_hi0 = (rh * D + (((dcol >> 3) ^ b_swz<D>(rh)) * 8) + (dcol & 7)) * 2;
   }
+  auto refresh_offsets = [&]() __attribute__((always_inline)) {
+    asm volatile("" : "+v"(a_off0), "+v"(tr_lo0), "+v"(tr_hi0));
+  };
 
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+  f32x16 s[NKB], dp[NKB];  // S^T and dP^T of the next tile (register r of block kb: key 32kb + 8(r/4) + 4h + r%4)
+  u32x4 dst[NT];           // dS^T of the current tile, bf16, as MFMA B operands (16-key steps)
 
-  auto tile = [&](int j, const int BUF, const bool MASKED) __attribute__((always_inline)) {
-    lds_cchar* kb_ = (lds_cchar*)(BUF ? k_lds1 : k_lds0);
-    lds_cchar* vb_ = (lds_cchar*)(BUF ? v_lds1 : v_lds0);
-    f32x16 s[2], dp[2];
+  // S^T = K Q^T and dP^T = V dO^T of the tile in buffer BUF (one LDS read
+  // per MFMA; the four accumulation chains alternate)
+  auto scores = [&](const int BUF) __attribute__((always_inline)) {
+    lds_cchar* kb_ = (lds_cchar*)kbuf(BUF);
+    lds_cchar* vb_ = (lds_cchar*)vbuf(BUF);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
       s[kb] = f32x16{};
       dp[kb] = f32x16{};
+    }
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 kf = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(kb_ + a_off[ks] + kb * 32 * D * 2);
-        const u32x4 vf = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(vb_ + a_off[ks] + kb * 32 * D * 2);
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const uint32_t ao = a_off0 ^ (32 * ks);
+        const u32x4 kf = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(kb_ + ao + kb * 32 * D * 2);
         s[kb] = mfma_32x32x16_bf16(kf, qf[ks], s[kb]);
+        const u32x4 vf = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(vb_ + ao + kb * 32 * D * 2);
         dp[kb] = mfma_32x32x16_bf16(vf, df[ks], dp[kb]);
       }
     }
-    // register r of block kb: key j0 + 32kb + 8(r/4) + 4h + r%4
-    const int j0 = j * BC;
-    const int lim = (CAUSAL ? min(a.Sk - 1, row + shift) : a.Sk - 1) - j0 - 4 * h;
-    u32x4 dst[4];
+  };
+  // dQ^T += K^T dS^T over the tile's 16-key steps (two transpose reads per
+  // MFMA)
+  auto dq_update = [&](const int BUF) __attribute__((always_inline)) {
+    lds_cchar* kb_ = (lds_cchar*)kbuf(BUF);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kb_ + (tr_lo0 ^ (64 * db)) + 16 * t * D * 2));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kb_ + (tr_hi0 ^ (64 * db)) + 16 * t * D * 2));
+        u32x4 af;
+        af[0] = __builtin_bit_cast(u32x2, lo)[0];
+        af[1] = __builtin_bit_cast(u32x2, lo)[1];
+        af[2] = __builtin_bit_cast(u32x2, hi)[0];
+        af[3] = __builtin_bit_cast(u32x2, hi)[1];
+        acc[db] = mfma_32x32x16_bf16(af, dst[t], acc[db]);
+      }
+    }
+  };
+  // dS^T = P^T * (dP^T - D) of tile jt from the score registers, with
+  // P^T = exp2(S^T c - LSE2); MASKED hides keys past the row's last visible
+  // key (causal diagonal, ragged tail)
+  auto dsoft = [&](int jt, const bool MASKED) __attribute__((always_inline)) {
+    const int lim = (CAUSAL ? min(a.Sk - 1, row + shift) : a.Sk - 1) - jt * BC - 4 * h;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
       const int kb = t >> 1, base = (t & 1) * 8;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -256,49 +350,104 @@ bwd_dq(BwdKArgs a) {
         dst[t][w] = pack_bf16x2(ds2[0], ds2[1]);
       }
     }
-    // dQ^T += K^T dS^T over the tile's 16-key steps
+  };
+  auto matrix_schedule = [&]() __attribute__((always_inline)) {
+    matrix_pipeline<0, 2 * NKB * KS, NT * NDB, kDqReadAhead, true>();
+  };
+
+  // Round j (P = j % S, a literal at every call).  Matrix phase: dQ_j from
+  // buffer P, then S, dP of tile j+1 from buffer (P+1) % S (unless j is the
+  // last tile; this order keeps dS_j and the new scores from being live
+  // together).  Vector phase: dS of tile j+1.  The leading group runs
+  //   issue(j) | matrix | barrier | vector | wait | barrier
+  // and the trailing group, whose phases sit one barrier later,
+  //   matrix | wait | barrier | issue(j+1) | vector | barrier;
+  // both groups issue round j's loads after the barrier that ends round
+  // j-1's matrix phase in both (the buffers of tile j-1 are then free), and
+  // before the barrier that precedes round j+1's matrix phase each wave
+  // waits for its loads of tile j+2 (those of earlier rounds).
+  auto round = [&](int j, const int P, const bool MASKED, const bool LEAD) __attribute__((always_inline)) {
+    const bool more = !MASKED || j + 1 < nkt;  // rounds of the plain loop always have a next tile
+    const bool next = more && (!MASKED || j + 1 < nneed);
+    if (LEAD) issue(j, P);
+    refresh_offsets();
+    if (!MASKED || j < nneed) dq_update(P);
+    if (next) scores((P + 1) % kDqStages);
+    if (!MASKED) matrix_schedule();
+    if (!LEAD) wait_vmem_at_most<kInFlight>();
+    lds_sync();
+    if (!LEAD) issue(j + 1, (P + 1) % kDqStages);
+    if (next) {
+      if (MASKED && j + 1 >= nfull)
+        dsoft(j + 1, true);
+      else
+        dsoft(j + 1, false);
+    }
+    if (LEAD) wait_vmem_at_most<kInFlight>();
+    lds_sync();
+  };
+
+  // the whole tile loop of one group (LEAD a literal: each group gets its
+  // own straight-line code, so the compiler sees which LDS buffer every read
+  // and every HBM->LDS load touches)
+  auto run = [&](const bool LEAD) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kb_ + tr_lo[db] + 16 * t * D * 2));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kb_ + tr_hi[db] + 16 * t * D * 2));
-        u32x4 af;
-        af[0] = __builtin_bit_cast(u32x2, lo)[0];
-        af[1] = __builtin_bit_cast(u32x2, lo)[1];
-        af[2] = __builtin_bit_cast(u32x2, hi)[0];
-        af[3] = __builtin_bit_cast(u32x2, hi)[1];
-        acc[db] = mfma_32x32x16_bf16(af, dst[t], acc[db]);
+    for (int t = 0; t + 1 < kDqStages; ++t) issue_tile(t, t);
+    wait_vmem_all();
+    lds_sync();
+    if (nneed > 0) {
+      scores(0);
+      if (LEAD) {
+        if (0 >= nfull)
+          dsoft(0, true);
+        else
+          dsoft(0, false);
       }
     }
+    lds_sync();
+    if (!LEAD) {
+      issue(0, 0);
+      if (nneed > 0) {
+        if (0 >= nfull)
+          dsoft(0, true);
+        else
+          dsoft(0, false);
+      }
+      lds_sync();
+    }
+    // rounds j < nplain produce an S_{j+1} that needs no mask for this
+    // wave; they run in a loop without masking code, the others (causal
+    // diagonal, ragged tail) in a second loop; unrolling by the stage count
+    // keeps buffer indices literal
+    const int nplain = max(min(nfull, nkt) - 1, 0);
+    int j = 0;
+    for (; j + kDqStages <= nplain; j += kDqStages) {
+#pragma unroll
+      for (int u = 0; u < kDqStages; ++u) round(j + u, u, false, LEAD);
+    }
+    for (; j < nkt; j += kDqStages) {
+      round(j, 0, true, LEAD);
+#pragma unroll
+      for (int u = 1; u < kDqStages; ++u)
+        if (j + u < nkt) round(j + u, u, true, LEAD);
+    }
+    if (LEAD) lds_sync();  // the trailing group's last barrier
+    wait_vmem_all();       // the zero-filling loads past the end
   };
 
   if (nkt > 0) {
-    issue(0, 0);
-    for (int j = 0; j < nkt; j += 2) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int jj = j + u;
-        if (jj < nkt) {
-          if (jj + 1 < nkt) {
-            issue(jj + 1, u ^ 1);
-            wait_vmem_at_most<2 * IPW>();
-          } else {
-            wait_vmem_all();
-          }
-          lds_sync();  // tile jj is in LDS for every wave
-          if (jj < nfull)
-            tile(jj, u, false);
-          else
-            tile(jj, u, true);
-          lds_sync();  // everyone is done with buffer u before it is refilled
-        }
-      }
-    }
+    if (lead)
+      run(true);
+    else
+      run(false);
   }
 
+  // the output address from an opaque copy of the row, so that it is not
+  // computed before the tile loop and held through it
+  int row_e = row;
+  asm volatile("" : "+v"(row_e));
   if (row_ok) {
-    uint16_t* out = a.dq + (rbase + row) * D;
+    uint16_t* out = a.dq + (rbase + row_e) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -619,7 +768,7 @@ hipError_t launch(const BwdArgs& p, hipStream_t s) {
   a.Hkv = p.Hkv;
   a.Sq = p.Sq;
   a.Sk = p.Sk;
-  a.nqb = (p.Sq + 127) / 128;
+  a.nqb = (p.Sq + kDqRows - 1) / kDqRows;
   a.nkb = (p.Sk + kKvKeys - 1) / kKvKeys;
   a.c2 = p.scale * kLog2e;
   a.scale = p.scale;
@@ -649,7 +798,7 @@ hipError_t launch(const BwdArgs& p, hipStream_t s) {
       grid_kv = (size_t)a.nstatic_kv + a.ndyn_kv;
     }
     if (rows > 0) {
-      hipLaunchKernelGGL((bwd_dq<D, CAUSAL>), dim3((unsigned)grid_q), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((bwd_dq<D, CAUSAL>), dim3((unsigned)grid_q), dim3(kDqThreads), 0, s, a);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

@@ -138,6 +138,32 @@ __device__ __forceinline__ T* uniform_ptr(T* p) {
   return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
 }
 
+// Scheduling pipeline of a matrix phase: KM MFMAs that take one LDS
+// operand read each (16-byte row reads) and VM MFMAs that take two
+// (transpose reads), the one-read group first unless TWO_FIRST, every read
+// issued L MFMAs ahead of the MFMA that consumes it, so LDS latency hides
+// behind matrix work.  The reads and MFMAs must appear in that order in
+// the code the phase is built from.
+template <int KM, int VM, bool TWO_FIRST>
+__device__ constexpr int reads_needed(int i) {  // reads consumed by MFMAs 0..i
+  if constexpr (TWO_FIRST) return i < VM ? 2 * (i + 1) : 2 * VM + (i - VM + 1);
+  return i < KM ? i + 1 : KM + 2 * (i - KM + 1);
+}
+template <int I, int KM, int VM, int L, bool TWO_FIRST = false>
+__device__ __forceinline__ void matrix_pipeline() {
+  if constexpr (I < KM + VM) {
+    constexpr int last = KM + VM - 1;
+    constexpr int hi = I + L < last ? I + L : last;
+    constexpr int lo = I == 0 ? 0
+                              : (I - 1 + L < last ? reads_needed<KM, VM, TWO_FIRST>(I - 1 + L)
+                                                  : reads_needed<KM, VM, TWO_FIRST>(last));
+    constexpr int n = reads_needed<KM, VM, TWO_FIRST>(hi) - lo;
+    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, 0);  // LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                        // one MFMA
+    matrix_pipeline<I + 1, KM, VM, L, TWO_FIRST>();
+  }
+}
+
 __device__ __forceinline__ int xcd_grouped_block(int bid, int nblocks) {
   constexpr int kXcds = 8;
   if (nblocks % kXcds != 0) return bid;

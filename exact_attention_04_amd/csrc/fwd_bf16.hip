@@ -104,26 +104,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Scheduling pipeline of a matrix phase: KM score MFMAs (one K read each)
-// then VM output MFMAs (two V transpose reads each), with the LDS reads
-// issued L MFMAs ahead of the MFMA that consumes them.
-template <int KM, int VM>
-__device__ constexpr int reads_needed(int i) {  // reads consumed by MFMAs 0..i
-  return i < KM ? i + 1 : KM + 2 * (i - KM + 1);
-}
-template <int I, int KM, int VM, int L>
-__device__ __forceinline__ void matrix_pipeline() {
-  if constexpr (I < KM + VM) {
-    constexpr int last = KM + VM - 1;
-    constexpr int hi = I + L < last ? I + L : last;
-    constexpr int lo = I == 0 ? 0 : (I - 1 + L < last ? reads_needed<KM, VM>(I - 1 + L) : reads_needed<KM, VM>(last));
-    constexpr int n = reads_needed<KM, VM>(hi) - lo;
-    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, 0);  // LDS reads
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                        // one MFMA
-    matrix_pipeline<I + 1, KM, VM, L>();
-  }
-}
-
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_kernel(FwdKernelArgs a) {

@@ -240,7 +240,7 @@ size_t attn_bwd_workspace_bytes(int B, int H, int Sq);
  * query sees get dK = dV = 0.  No atomics: results are deterministic.
  * dtype must be ATTN_BF16; d in {64, 128}; Sq, Sk <= 2^30; causal is
  * bottom-right aligned.  Errors as for attn_fwd, plus ATTN_ERR_WORKSPACE.
- * Work order: in a causal call with at least 32 blocks of 128 query rows (a
+ * Work order: in a causal call with at least 32 blocks of 256 query rows (a
  * multiple of 4) and B*H a multiple of 8, or at least 16 blocks of 256 keys
  * (a multiple of 4) and B*Hkv a multiple of 8, the lightest quarter of those
  * blocks is claimed at run time through counters in a static device array,

@@ -195,13 +195,14 @@ def test_bwd_full_size_every_head(part):
 
 @pytest.mark.parametrize("H,Hkv", [(8, 8), (16, 8)])
 def test_bwd_dynamic_tail_equals_captured_fixed_order(H, Hkv):
-    """With 32+ query blocks and 16+ key blocks the lightest quarter of each
-    kernel's blocks is claimed at run time; a call captured into a graph runs
-    the fixed order.  Same arithmetic per block, so the gradients must agree
-    bit for bit, on every replay, with eager calls between the replays."""
+    """With 32+ query blocks of 256 rows and 16+ key blocks of 256 keys the
+    lightest quarter of each kernel's blocks is claimed at run time (S = 8192
+    qualifies for both); a call captured into a graph runs the fixed order.
+    Same arithmetic per block, so the gradients must agree bit for bit, on
+    every replay, with eager calls between the replays."""
     from exact_attention_04_amd import binding
     rng = np.random.default_rng(70 + H)
-    S, d = 4096, 128
+    S, d = 8192, 128
     q = synth.normal(rng, (1, H, S, d), "bf16").cuda()
     k = synth.normal(rng, (1, Hkv, S, d), "bf16").cuda()
     v = synth.normal(rng, (1, Hkv, S, d), "bf16").cuda()

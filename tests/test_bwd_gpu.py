@@ -111,9 +111,15 @@ def test_bwd_matches_oracle(B, H, Hkv, Sq, Sk, d, causal):
     bwd_case(11 + Sq + Sk + d, B, H, Hkv, Sq, Sk, d, causal, what="small")
 
 
-def test_bwd_larger_sequence():
-    """Two heads at 2048 tokens: 16 query blocks, 16 key blocks."""
-    bwd_case(5, 1, 2, 2, 2048, 2048, 128, True, what="2k")
+@pytest.mark.parametrize("H,Hkv,Sq,Sk,d,causal", [
+    (2, 2, 2048, 2048, 128, True),   # 8 query blocks of 256 rows, 64 key tiles of 32, 8 key blocks of 256
+    (2, 1, 2048, 2048, 64, True),    # d = 64: key tiles of 64, grouped-query heads
+    (2, 2, 1000, 1500, 128, False),  # ragged query block and key tile, a long unmasked run
+])
+def test_bwd_larger_sequence(H, Hkv, Sq, Sk, d, causal):
+    """Sequences long enough that every pipeline buffer of both kernels is
+    reused many times, against the oracle on every element."""
+    bwd_case(5 + Sq + d, 1, H, Hkv, Sq, Sk, d, causal, what="long")
 
 
 def test_bwd_empty_query_or_key_side():

@@ -124,23 +124,20 @@ bwd_dq(BwdKArgs a) {
   static_assert(IPW >= 1, "every wave loads part of each tile");
   // one LDS object per buffer, so the compiler can prove that loads into one
   // buffer never alias reads of another
-  static_assert(kDqStages >= 3 && kDqStages <= 5, "three to five buffers per stream");
-  constexpr int T3 = kDqStages > 3 ? TILE : 1, T4 = kDqStages > 4 ? TILE : 1;
+  static_assert(kDqStages == 4, "one LDS object per buffer below");
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds2[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t k_lds3[T3];
-  __shared__ __attribute__((aligned(1024))) uint16_t k_lds4[T4];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds3[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds2[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds3[T3];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds4[T4];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds3[TILE];
   auto kbuf = [&](const int I) __attribute__((always_inline)) {
-    return I == 0 ? k_lds0 : I == 1 ? k_lds1 : I == 2 ? k_lds2 : I == 3 ? k_lds3 : k_lds4;
+    return I == 0 ? k_lds0 : I == 1 ? k_lds1 : I == 2 ? k_lds2 : k_lds3;
   };
   auto vbuf = [&](const int I) __attribute__((always_inline)) {
-    return I == 0 ? v_lds0 : I == 1 ? v_lds1 : I == 2 ? v_lds2 : I == 3 ? v_lds3 : v_lds4;
+    return I == 0 ? v_lds0 : I == 1 ? v_lds1 : I == 2 ? v_lds2 : v_lds3;
   };
   typedef const __attribute__((address_space(3))) char lds_cchar;
 

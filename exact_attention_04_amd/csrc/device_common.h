@@ -124,9 +124,6 @@ __device__ __forceinline__ void wait_vmem_at_most() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// Workgroup index remapped so that the workgroups the hardware sends to one
-// XCD (dispatch is round-robin over the 8 XCDs) get consecutive logical ids:
-// neighbouring tiles of one head then share that XCD's L2.
 // A wave-uniform value the compiler cannot prove uniform, moved to scalar
 // registers (buffer descriptors built from it then need no per-lane loop).
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -164,6 +161,9 @@ __device__ __forceinline__ void matrix_pipeline() {
   }
 }
 
+// Workgroup index remapped so that the workgroups the hardware sends to one
+// XCD (dispatch is round-robin over the 8 XCDs) get consecutive logical ids:
+// neighbouring tiles of one head then share that XCD's L2.
 __device__ __forceinline__ int xcd_grouped_block(int bid, int nblocks) {
   constexpr int kXcds = 8;
   if (nblocks % kXcds != 0) return bid;

@@ -58,7 +58,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   if (lse != nullptr && !aligned4(lse)) return ATTN_ERR_INVALID_ARG;
   if (nq == 0) return ATTN_OK;
 
-  attn::FwdArgs a;
+  attn::FwdArgs a{};  // every field zero/null until set
   a.q = q;
   a.k = k;
   a.v = v;
@@ -114,7 +114,7 @@ int verify_contiguous(const void* q, const void* k_cache, const void* v_cache, c
   }
   if (nq == 0) return ATTN_OK;
 
-  attn::VerifyArgs a;
+  attn::VerifyArgs a{};  // every field zero/null until set
   a.q = q;
   a.k = k_cache;
   a.v = v_cache;
@@ -200,7 +200,7 @@ extern "C" int attn_verify_paged(const void* q, const void* k_pages, const void*
   if (need > 0 && (workspace == nullptr || !aligned16(workspace))) return ATTN_ERR_INVALID_ARG;
   if (nq == 0) return ATTN_OK;
 
-  attn::VerifyArgs a;
+  attn::VerifyArgs a{};  // every field zero/null until set
   a.q = q;
   a.k = k_pages;
   a.v = v_pages;
@@ -250,7 +250,7 @@ extern "C" int attn_spec_accept(const int32_t* draft_tokens, const float* draft_
   const size_t need = attn::spec_accept_workspace_bytes(B, V);
   if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 7u) != 0) return ATTN_ERR_INVALID_ARG;
-  attn::SpecAcceptArgs a;
+  attn::SpecAcceptArgs a{};  // every field zero/null until set
   a.draft_tokens = draft_tokens;
   a.draft_probs = draft_probs;
   a.target_probs = target_probs;
@@ -292,7 +292,7 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (need > 0 && (workspace == nullptr || !aligned16(workspace))) return ATTN_ERR_INVALID_ARG;
   if (nq == 0 && nk == 0) return ATTN_OK;
-  attn::BwdArgs a;
+  attn::BwdArgs a{};  // every field zero/null until set
   a.q = q;
   a.k = k;
   a.v = v;

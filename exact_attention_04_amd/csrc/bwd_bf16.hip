@@ -750,7 +750,7 @@ TailPoolState g_bwd_tail[kTailMaxDevices];
 
 template <int D, bool CAUSAL>
 hipError_t launch(const BwdArgs& p, hipStream_t s) {
-  BwdKArgs a;
+  BwdKArgs a{};  // every field zero/null until set
   const size_t rows = (size_t)p.B * p.H * p.Sq;
   a.q = static_cast<const uint16_t*>(p.q);
   a.k = static_cast<const uint16_t*>(p.k);

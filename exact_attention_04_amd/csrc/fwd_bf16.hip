@@ -532,7 +532,7 @@ TailPoolState g_fwd_tail[kTailMaxDevices];
 
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& p, hipStream_t s) {
-  FwdKernelArgs a;
+  FwdKernelArgs a{};  // every field zero/null until set
   a.q = static_cast<const uint16_t*>(p.q);
   a.k = static_cast<const uint16_t*>(p.k);
   a.v = static_cast<const uint16_t*>(p.v);

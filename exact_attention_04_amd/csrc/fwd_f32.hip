@@ -176,7 +176,7 @@ __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(F32Args a) {
 
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& p, hipStream_t s) {
-  F32Args a;
+  F32Args a{};  // every field zero/null until set
   a.q = static_cast<const float*>(p.q);
   a.k = static_cast<const float*>(p.k);
   a.v = static_cast<const float*>(p.v);

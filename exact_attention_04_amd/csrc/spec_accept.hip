@@ -264,7 +264,7 @@ static size_t spec_sums_bytes(int B, int V) {
 size_t spec_accept_workspace_bytes(int B, int V) { return spec_sums_bytes(B, V) + (size_t)B * sizeof(int32_t); }
 
 hipError_t launch_spec_accept(const SpecAcceptArgs& p, hipStream_t s) {
-  SpecArgs a;
+  SpecArgs a{};  // every field zero/null until set
   a.draft = p.draft_tokens;
   a.q = p.draft_probs;
   a.p = p.target_probs;

@@ -616,7 +616,7 @@ hipError_t launch(const VerifyArgs& p, hipStream_t s) {
   float* part_lse = reinterpret_cast<float*>(ws + align_up(n_parts * D * 4));
   int32_t* seg_np = reinterpret_cast<int32_t*>(ws + align_up(n_parts * D * 4) + align_up(n_parts * 4));
 
-  SplitArgs sa;
+  SplitArgs sa{};  // every field zero/null until set
   sa.q = static_cast<const uint16_t*>(p.q);
   sa.k = static_cast<const uint16_t*>(p.k);
   sa.v = static_cast<const uint16_t*>(p.v);
@@ -644,7 +644,7 @@ hipError_t launch(const VerifyArgs& p, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  MergeArgs ma;
+  MergeArgs ma{};  // every field zero/null until set
   ma.part_o = part_o;
   ma.part_lse = part_lse;
   ma.seg_np = seg_np;

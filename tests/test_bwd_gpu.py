@@ -115,6 +115,7 @@ def test_bwd_matches_oracle(B, H, Hkv, Sq, Sk, d, causal):
     (2, 2, 2048, 2048, 128, True),   # 8 query blocks of 256 rows, 64 key tiles of 32, 8 key blocks of 256
     (2, 1, 2048, 2048, 64, True),    # d = 64: key tiles of 64, grouped-query heads
     (2, 2, 1000, 1500, 128, False),  # ragged query block and key tile, a long unmasked run
+    (3, 1, 3000, 3000, 128, True),   # 36 blocks per kernel, not a multiple of the XCD count
 ])
 def test_bwd_larger_sequence(H, Hkv, Sq, Sk, d, causal):
     """Sequences long enough that every pipeline buffer of both kernels is

@@ -86,6 +86,14 @@ def test_full_size_every_row(name, part):
     P.log(f"    ok {len(pairs)} heads x {w.Sq} rows {res}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_long_sequence_plain_order_every_row(d):
+    """Long causal rows whose block count (3 heads x 31 blocks) is not a
+    multiple of the XCD count: no head pairs, no dynamic tail, workgroups in
+    launch order.  Every row of every head against the oracle."""
+    P.fwd_case(7900 + d, 1, 3, 1, 7900, 7900, d, True, "bf16", what="plain order")
+
+
 @pytest.mark.parametrize("Sq,Sk", [(8192, 8192), (8000, 8192)])
 def test_head_pairs_order_every_row(Sq, Sk):
     """32+ query blocks per head: the workgroups run two heads at a time in
